@@ -1,0 +1,28 @@
+"""CPU oracle for the DSA indexer -> top-k -> sparse MLA attention path under IndexCache.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke entry point and the
+benchmark's CPU-baseline leg may import this package.  The product path (the HIP
+library and its Python binding) never imports, links or calls it, and shares no
+code, table or helper with it.
+
+Everything is plain NumPy in float64, evaluated row by row straight from the
+definitions on the source pages.  Citations use two page titles:
+
+  [IDX] Jerry's Blog, "注意力机制中的 Index：从位置下标到预算检索"
+        (attention indices: dense attention §1, sparse attention §2, the top-k
+        error decomposition §3, DeepSeek-V3.2 lightning indexer §4, GLM-5 index
+        mask and deterministic top-k §6.4-§6.5, index-quality metrics §8)
+  [IC]  "读懂 IndexCache：从 DSA 的选词开销到跨层索引复用"
+        (F/S layer roles §1.1, the cache update loop and the {2,5,8} example §1.2)
+
+Every function here is pinned by tests under tests/ against closed forms,
+hand-derived fixtures, brute force and library routines (see test_oracle_*.py).
+"""
+from .formats import decode_bf16, decode_e4m3fn, e4m3fn_table, dequant_rows
+from .dsa import (indexer_row, indexer_row_int2, topk_row, attn_row, dense_attn_row,
+                  indexcache_plan, indexcache_forward, RoleError, tolerance_row,
+                  captured_mass, overlap)
+
+__all__ = ["decode_bf16", "decode_e4m3fn", "e4m3fn_table", "dequant_rows", "indexer_row",
+           "indexer_row_int2", "topk_row", "attn_row", "dense_attn_row", "indexcache_plan",
+           "indexcache_forward", "RoleError", "tolerance_row", "captured_mass", "overlap"]
