@@ -1,0 +1,251 @@
+"""Benchmark of the DSA hot path on one MI355X.
+
+Default workload: the 4-layer FSSS prefill stack at L = 200,000 (fp8 e4m3 indexer
+inputs with per-row scales, H^I = 64 x d_I = 128, k = 2048; sparse MLA attention
+with 128 heads over a [L, 576] bf16 latent), processed in 8192-query chunks
+(chunked prefill: every layer of a chunk before the next chunk).  One step = one
+indexcache_forward call over the whole stack: the F layer scores and selects,
+all four layers attend.  Inputs are synthetic, seeded, and already resident in
+HBM when the timed region starts; each layer's fp32 output goes to a ring of one
+chunk (the next layer of a real model would consume it chunk by chunk).
+
+Prints one JSON line.  `value` = queries per second through the whole step.
+Per-launch durations come from HIP events that the library records around each
+indexer / attention call on the stream it launches on, inside the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2.5e15, "fp8": 5.0e15, "hbm": 8.0e12}   # MI355X dense MFMA, HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=4, help="synthetic workload id (4 = L=200K FSSS fp8)")
+    ap.add_argument("--L", type=int, default=None, help="override the context length (development only)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-all-f", action="store_true", help="skip the all-F comparison step")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+class Hip:
+    """Minimal HIP event plumbing (timing only)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for j in range(n):
+            e = ctypes.c_void_p()
+            assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+            arr[j] = e
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        f = ctypes.c_float()
+        assert self.h.hipEventSynchronize(b) == 0
+        assert self.h.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return float(f.value)
+
+
+def pairs_in_chunk(r0, r1, k):
+    """Visible (query, key) pairs and selected pairs of query rows [r0, r1) of one sequence."""
+    t = np.arange(r0, r1, dtype=np.float64)
+    return float((t + 1).sum()), float(np.minimum(t + 1, k).sum())
+
+
+def cpu_baseline(layers_host, roles, L, k, scale, seconds):
+    """The oracle as it stands, timed on this host on a bounded sample of rows of the same stack.
+
+    Rows are drawn uniformly over [0, L) so their mean cost matches the full
+    workload's (the indexer cost of row t grows with t).  Returns queries/s."""
+    import oracle
+    threads = len(os.sched_getaffinity(0))
+    g = np.random.default_rng(1234)
+    done, t0 = 0, time.perf_counter()
+    keys = layers_host["keys"]
+    while time.perf_counter() - t0 < seconds:
+        t = int(g.integers(0, L))
+        T = None
+        for l, role in enumerate(roles):
+            if role == "F":
+                I = oracle.indexer_row(layers_host["q_idx"][l](t), layers_host["w"][l](t), keys[l][: t + 1])
+                T = oracle.topk_row(I, k)[0]
+            sel = T[T >= 0]
+            lat = layers_host["latent"][l](sel)
+            oracle.attn_row(layers_host["q"][l](t), lat, np.arange(sel.size), scale, 512)
+        done += 1
+    dt = time.perf_counter() - t0
+    return done / dt, done, dt, threads
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import dsa_indexer_indexcache_amd as dsa
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    assert wl.decode_B == 0, "the bench times a prefill stack"
+    L = wl.L if args.L is None else args.L
+    roles, k, dev = wl.roles, wl.k, "cuda"
+    chunk = min(wl.q_chunk, L)
+    torch.cuda.init()
+    dsa.lib()
+
+    layers = []
+    for l in range(len(roles)):
+        li = synth.workload_layer(args.workload, l, device=dev, L=L)
+        layers.append(li)
+    torch.cuda.synchronize()
+    n_chunks = (L + chunk - 1) // chunk
+    outs = [torch.empty((chunk, wl.n_h, 512), dtype=torch.float32, device=dev) for _ in roles]
+    index_cache = torch.empty((chunk, k), dtype=torch.int32, device=dev)
+    ldicts = [dsa.layer_dict(x) for x in layers]
+    hip = Hip()
+    n_calls = n_chunks * len(roles) + n_chunks * roles.count("F")
+    ev_steps = [hip.events(2 * n_calls) for _ in range(args.steps)]   # read only after the timed region
+
+    def step(rl, events=None):
+        return dsa.indexcache_forward(rl, ldicts, k, q_chunk=chunk, index_rows=chunk, out_rows=chunk,
+                                      outs=outs, index_cache=index_cache, events=events)
+
+    for _ in range(args.warmup):
+        step(roles)
+    torch.cuda.synchronize()
+
+    kind_ms = {0: [], 1: []}
+    traces = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        traces.append(step(roles, ev_steps[s_]).trace)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    for s_, tr in enumerate(traces):
+        evs = ev_steps[s_]
+        for j, (kind, layer, ch) in enumerate(tr):
+            kind_ms[kind].append((ch, hip.elapsed_ms(evs[2 * j], evs[2 * j + 1])))
+
+    # algorithmic work per chunk
+    qk_flops_pair = 2.0 * wl.H * wl.d
+    attn_flops_pair = wl.n_h * 2.0 * (576 + 512)
+    idx_ms = sum(ms for _, ms in kind_ms[0]) / args.steps
+    attn_ms = sum(ms for _, ms in kind_ms[1]) / args.steps
+    idx_flops = attn_flops = 0.0
+    for c in range(n_chunks):
+        vis, sel = pairs_in_chunk(c * chunk, min(L, (c + 1) * chunk), k)
+        idx_flops += qk_flops_pair * vis * roles.count("F")
+        attn_flops += attn_flops_pair * sel * len(roles)
+    idx_peak = PEAK["fp8" if wl.qk_dtype == "fp8" else "bf16"]
+    idx_tfs = idx_flops / (idx_ms * 1e-3) / 1e12
+    attn_tfs = attn_flops / (attn_ms * 1e-3) / 1e12
+    comp = {
+        "indexer_topk": {"ms_per_step": idx_ms, "launches_per_step": len(kind_ms[0]) // args.steps,
+                         "queries_per_s": L * roles.count("F") / (idx_ms * 1e-3),
+                         "achieved_tflops": idx_tfs, "peak_tflops": idx_peak / 1e12,
+                         "frac": idx_tfs * 1e12 / idx_peak},
+        "sparse_attn": {"ms_per_step": attn_ms, "launches_per_step": len(kind_ms[1]) // args.steps,
+                        "tok_per_s": L * len(roles) / (attn_ms * 1e-3),
+                        "achieved_tflops": attn_tfs, "peak_tflops": PEAK["bf16"] / 1e12,
+                        "frac": attn_tfs * 1e12 / PEAK["bf16"]},
+    }
+    dom = "sparse_attn" if attn_ms >= idx_ms else "indexer_topk"
+    dc = comp[dom]
+    launches = dc["launches_per_step"]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": dc["achieved_tflops"], "peak": dc["peak_tflops"],
+                "unit": "TFLOP/s", "frac": dc["frac"], "traffic": None,
+                "avg_launch_ms": dc["ms_per_step"] / max(launches, 1),
+                "work_per_launch_tflop": (attn_flops if dom == "sparse_attn" else idx_flops) / max(launches, 1) / 1e12}
+
+    extra = {}
+    if not args.no_all_f and "S" in roles:
+        allf = "F" * len(roles)
+        step(allf)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ev_allf = hip.events(2 * n_chunks * 2 * len(roles))
+        res = step(allf, ev_allf)
+        torch.cuda.synchronize()
+        t_allf = time.perf_counter() - t1
+        idx_allf = sum(hip.elapsed_ms(ev_allf[2 * j], ev_allf[2 * j + 1])
+                       for j, (kd, _, _) in enumerate(res.trace) if kd == 0)
+        extra = {"all_f_ms_per_step": 1e3 * t_allf, "all_f_indexer_ms": idx_allf,
+                 "indexer_time_ratio_allF_over_pattern": idx_allf / idx_ms,
+                 "step_speedup_pattern_vs_allF": 1e3 * t_allf / ms_step,
+                 "indexer_work_saved": 1.0 - roles.count("F") / len(roles)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle import formats
+
+        def deq_rows(t, s, rows):
+            r = torch.as_tensor(np.atleast_1d(rows), device=dev)
+            if t.dtype == torch.float8_e4m3fn:
+                return formats.dequant_rows(synth.bits(t[r]), synth.bits(s[r]), "fp8")
+            return formats.decode_bf16(synth.bits(t[r]))
+
+        host = {"keys": [], "q_idx": [], "w": [], "q": [], "latent": []}
+        for l, li in enumerate(layers):
+            if roles[l] == "F":
+                kk = li.k_idx
+                host["keys"].append(formats.dequant_rows(synth.bits(kk), synth.bits(li.k_scale), "fp8")
+                                    if kk.dtype == torch.float8_e4m3fn else formats.decode_bf16(synth.bits(kk)))
+            else:
+                host["keys"].append(None)
+            host["q_idx"].append(lambda t, li=li: deq_rows(li.q_idx, li.q_scale, t)[0])
+            host["w"].append(lambda t, li=li: formats.decode_bf16(synth.bits(li.w[t:t + 1]))[0])
+            host["q"].append(lambda t, li=li: formats.decode_bf16(synth.bits(li.q[t:t + 1]))[0])
+            lat_bits = synth.bits(li.latent)      # host copy before timing: the oracle reads host memory
+            host["latent"].append(lambda rows, b=lat_bits: formats.decode_bf16(b[rows]))
+        qps, nrows, secs, threads = cpu_baseline(host, roles, L, k, wl.scale, args.cpu_seconds)
+        cpu = {"value": qps, "unit": "queries/s", "cores": threads, "kind": "oracle",
+               "sample": "%d query rows drawn uniformly over [0, %d) through the %s stack (fp64 NumPy indexer, "
+                         "sort top-k, sparse attention), %.1f s" % (nrows, L, roles, secs)}
+
+    line = {
+        "metric": "indexer+top-k queries/s & sparse-attn tok/s at L=200K; % MFMA/HBM peak",
+        "value": L / (ms_step * 1e-3),
+        "unit": "queries/s (whole %s step)" % roles,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 indexer / bf16 attention, fp32 accumulate" if wl.qk_dtype == "fp8" else "bf16, fp32 accumulate",
+        "data": "synthetic (seeded, shapes of the DSA/IndexCache pages' 200K-context setting)",
+        "config": {"workload": wl.name, "L": L, "roles": roles, "k": k, "H_idx": wl.H, "d_idx": wl.d,
+                   "n_h": wl.n_h, "q_chunk": chunk, "parallelism": "single GPU"},
+        "components": comp,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,295 @@
+"""MI355X (gfx950) DSA hot path: lightning indexer + top-k + sparse MLA attention under IndexCache.
+
+Thin Python binding over the C ABI in include/dsa.h (libdsa_mi355x.so, built
+in-tree by build.py).  This module only marshals arguments: torch supplies
+device memory and the stream; every step of the path runs in the HIP kernels.
+There is no CPU or eager fallback: if the library is missing or a call fails,
+an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, List, Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa_mi355x.so")
+
+DSA_BF16, DSA_FP8_E4M3, DSA_FP32 = 0, 1, 2
+DSA_MAX_B = 64
+DSA_MAX_LAYERS = 256
+STATUS = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_ROLES", -3: "DSA_ERR_FIRST_NOT_F",
+          -4: "DSA_ERR_UNSUPPORTED", -5: "DSA_ERR_ALIGNMENT", -6: "DSA_ERR_WORKSPACE", -7: "DSA_ERR_HIP"}
+
+EXPORTS = ("dsa_indexer_topk", "dsa_indexer_topk_ws", "dsa_sparse_attn", "dsa_sparse_attn_ws",
+           "indexcache_forward", "indexcache_forward_ws", "indexcache_plan", "dsa_status_string",
+           "dsa_last_error", "dsa_version")
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__("%s (%d): %s" % (STATUS.get(status, "?"), status, detail))
+        self.status = status
+
+
+class Seqs(ctypes.Structure):
+    """dsa_seqs: packed variable-length batch (see include/dsa.h)."""
+    _fields_ = [("B", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("q_start", ctypes.c_int64 * (DSA_MAX_B + 1)),
+                ("k_start", ctypes.c_int64 * (DSA_MAX_B + 1)),
+                ("q_pos0", ctypes.c_int64 * DSA_MAX_B)]
+
+    @classmethod
+    def varlen(cls, q_lens: Sequence[int], k_lens: Sequence[int], q_pos0: Sequence[int]) -> "Seqs":
+        s = cls()
+        B = len(q_lens)
+        if not (1 <= B <= DSA_MAX_B) or len(k_lens) != B or len(q_pos0) != B:
+            raise ValueError("need 1..%d sequences with matching lengths" % DSA_MAX_B)
+        s.B = B
+        qa = ka = 0
+        for b in range(B):
+            s.q_start[b] = qa
+            s.k_start[b] = ka
+            s.q_pos0[b] = int(q_pos0[b])
+            qa += int(q_lens[b])
+            ka += int(k_lens[b])
+        s.q_start[B] = qa
+        s.k_start[B] = ka
+        return s
+
+    @classmethod
+    def prefill(cls, n_q: int, n_k: Optional[int] = None, q_pos0: int = 0) -> "Seqs":
+        """One sequence: n_q queries at positions q_pos0.. over n_k keys (default n_k = q_pos0 + n_q)."""
+        return cls.varlen([n_q], [q_pos0 + n_q if n_k is None else n_k], [q_pos0])
+
+    @classmethod
+    def decode(cls, lens: Iterable[int]) -> "Seqs":
+        """B sequences, one new query each at position len_b - 1 (the caches already hold it)."""
+        lens = [int(x) for x in lens]
+        return cls.varlen([1] * len(lens), lens, [x - 1 for x in lens])
+
+    @property
+    def n_q(self) -> int:
+        return int(self.q_start[self.B])
+
+    @property
+    def n_k(self) -> int:
+        return int(self.k_start[self.B])
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("q_idx", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k_idx", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("w", ctypes.c_void_p), ("q", ctypes.c_void_p),
+                ("latent", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("d", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("n_h", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("qk_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("q_chunk", ctypes.c_int64), ("index_rows", ctypes.c_int64),
+                ("out_rows", ctypes.c_int64)]
+
+
+DSA_MAX_TRACE = 1024
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("events", ctypes.c_void_p), ("event_cap", ctypes.c_int32), ("n_layers", ctypes.c_int32),
+                ("n_indexer_calls", ctypes.c_int32), ("n_chunks", ctypes.c_int32), ("n_traced", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("src_layer", ctypes.c_int32 * DSA_MAX_LAYERS),
+                ("trace_kind", ctypes.c_int8 * DSA_MAX_TRACE), ("trace_layer", ctypes.c_int16 * DSA_MAX_TRACE),
+                ("trace_chunk", ctypes.c_int32 * DSA_MAX_TRACE)]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("HIP library %s is missing: run `python -m dsa_indexer_indexcache_amd.build` "
+                               "(or __graft_entry__.build())" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_float
+        L.dsa_indexer_topk.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.POINTER(Seqs), vp, vp, vp,
+                                       sz, vp]
+        L.dsa_indexer_topk.restype = i32
+        L.dsa_indexer_topk_ws.argtypes = [i32, i32, i32, i32, ctypes.POINTER(Seqs)]
+        L.dsa_indexer_topk_ws.restype = sz
+        L.dsa_sparse_attn.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, ctypes.POINTER(Seqs), vp, i32, vp, sz,
+                                      vp]
+        L.dsa_sparse_attn.restype = i32
+        L.dsa_sparse_attn_ws.argtypes = [i32, i32, i32, i32, ctypes.POINTER(Seqs)]
+        L.dsa_sparse_attn_ws.restype = sz
+        L.indexcache_forward.argtypes = [ctypes.c_char_p, ctypes.POINTER(Layer), ctypes.POINTER(Shape),
+                                         ctypes.POINTER(Seqs), vp, vp, vp, sz, ctypes.POINTER(Stats), vp]
+        L.indexcache_forward.restype = i32
+        L.indexcache_forward_ws.argtypes = [ctypes.c_char_p, ctypes.POINTER(Shape), ctypes.POINTER(Seqs)]
+        L.indexcache_forward_ws.restype = sz
+        L.indexcache_plan.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+        L.indexcache_plan.restype = i32
+        L.dsa_status_string.argtypes = [i32]
+        L.dsa_status_string.restype = ctypes.c_char_p
+        L.dsa_last_error.argtypes = []
+        L.dsa_last_error.restype = ctypes.c_char_p
+        L.dsa_version.argtypes = []
+        L.dsa_version.restype = i32
+        _lib_handle = L
+    return _lib_handle
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise DsaError(rc, lib().dsa_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return DSA_FP8_E4M3
+    raise TypeError("indexer tensors must be bfloat16 or float8_e4m3fn, got %s" % t.dtype)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _workspace(nbytes: int, device) -> Optional[torch.Tensor]:
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def indexcache_plan(roles: str):
+    """Host-only plan: (src_layer list, number of indexer calls); raises DsaError on a bad role string."""
+    n = len(roles)
+    src = (ctypes.c_int32 * max(n, 1))()
+    calls = ctypes.c_int32(0)
+    _check(lib().indexcache_plan(roles.encode(), src, ctypes.byref(calls)))
+    return [int(src[i]) for i in range(n)], int(calls.value)
+
+
+def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, k: int, seqs: Optional[Seqs] = None,
+                 q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+                 want_scores: bool = False, idx_out: Optional[torch.Tensor] = None,
+                 score_out: Optional[torch.Tensor] = None, stream=None):
+    """dsa_indexer_topk: returns (idx int32 [n_q, k], scores fp32 [n_q, k] or None)."""
+    n_q, H, d = q_idx.shape
+    if seqs is None:
+        seqs = Seqs.prefill(n_q, k_idx.shape[0], q_pos0=k_idx.shape[0] - n_q)
+    dt = _dtype_code(q_idx)
+    dev = q_idx.device
+    if idx_out is None:
+        idx_out = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    if want_scores and score_out is None:
+        score_out = torch.empty((n_q, k), dtype=torch.float32, device=dev)
+    L = lib()
+    nbytes = L.dsa_indexer_topk_ws(dt, H, d, k, ctypes.byref(seqs))
+    ws = _workspace(nbytes, dev)
+    _check(L.dsa_indexer_topk(_ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w), dt, H, d, k,
+                              ctypes.byref(seqs), _ptr(idx_out), _ptr(score_out), _ptr(ws), nbytes, _stream(stream)))
+    return idx_out, score_out
+
+
+def sparse_attn(q: torch.Tensor, latent: torch.Tensor, idx: torch.Tensor, seqs: Optional[Seqs] = None,
+                scale: Optional[float] = None, d_v: int = 512, out_dtype=torch.float32,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """dsa_sparse_attn: out [n_q, n_h, d_v] (fp32 by default)."""
+    n_q, n_h, d_qk = q.shape
+    k = idx.shape[1]
+    if seqs is None:
+        seqs = Seqs.prefill(n_q, latent.shape[0], q_pos0=latent.shape[0] - n_q)
+    if scale is None:
+        scale = d_qk ** -0.5
+    odt = DSA_FP32 if out_dtype == torch.float32 else DSA_BF16
+    if out is None:
+        out = torch.empty((n_q, n_h, d_v), dtype=out_dtype, device=q.device)
+    L = lib()
+    nbytes = L.dsa_sparse_attn_ws(n_h, d_qk, d_v, k, ctypes.byref(seqs))
+    ws = _workspace(nbytes, q.device)
+    _check(L.dsa_sparse_attn(_ptr(q), _ptr(latent), _ptr(idx), n_h, d_qk, d_v, k, float(scale), ctypes.byref(seqs),
+                             _ptr(out), odt, _ptr(ws), nbytes, _stream(stream)))
+    return out
+
+
+class ForwardResult:
+    def __init__(self, outs, index_cache, score_cache, stats: Stats):
+        self.outs = outs
+        self.index_cache = index_cache
+        self.score_cache = score_cache
+        self.n_indexer_calls = int(stats.n_indexer_calls)
+        self.n_chunks = int(stats.n_chunks)
+        self.src_layer = [int(stats.src_layer[i]) for i in range(stats.n_layers)]
+        self.trace = [(int(stats.trace_kind[j]), int(stats.trace_layer[j]), int(stats.trace_chunk[j]))
+                      for j in range(stats.n_traced)]
+
+
+def indexcache_forward(roles: str, layers: Sequence[dict], k: int, seqs: Optional[Seqs] = None,
+                       q_chunk: Optional[int] = None, index_rows: Optional[int] = None,
+                       out_rows: Optional[int] = None, scale: Optional[float] = None, d_v: int = 512,
+                       out_dtype=torch.float32, want_scores: bool = False, outs: Optional[List[torch.Tensor]] = None,
+                       index_cache: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                       events=None, stream=None) -> ForwardResult:
+    """indexcache_forward over layers given as dicts of tensors
+    {q_idx, q_scale, k_idx, k_scale, w, q, latent} (indexer tensors needed on F layers only)."""
+    n_layers = len(roles)
+    if len(layers) != n_layers:
+        raise ValueError("one layer dict per role")
+    l0 = layers[0]
+    n_q, n_h, d_qk = l0["q"].shape
+    dev = l0["q"].device
+    f0 = next(i for i, r in enumerate(roles) if r == "F") if "F" in roles else 0
+    qi = layers[f0].get("q_idx")
+    if seqs is None:
+        seqs = Seqs.prefill(n_q, l0["latent"].shape[0], q_pos0=l0["latent"].shape[0] - n_q)
+    shape = Shape()
+    shape.H, shape.d = (qi.shape[1], qi.shape[2]) if qi is not None else (0, 0)
+    shape.k, shape.n_h, shape.d_qk, shape.d_v = k, n_h, d_qk, d_v
+    shape.scale = float(d_qk ** -0.5 if scale is None else scale)
+    shape.qk_dtype = _dtype_code(qi) if qi is not None else DSA_BF16
+    shape.out_dtype = DSA_FP32 if out_dtype == torch.float32 else DSA_BF16
+    shape.q_chunk = int(q_chunk or max(n_q, 1))
+    shape.index_rows = int(index_rows or max(n_q, 1))
+    shape.out_rows = int(out_rows or max(n_q, 1))
+    if outs is None:
+        outs = [torch.empty((shape.out_rows, n_h, d_v), dtype=out_dtype, device=dev) for _ in range(n_layers)]
+    if index_cache is None:
+        index_cache = torch.empty((shape.index_rows, k), dtype=torch.int32, device=dev)
+    score_cache = torch.empty((shape.index_rows, k), dtype=torch.float32, device=dev) if want_scores else None
+    arr = (Layer * n_layers)()
+    for l, d in enumerate(layers):
+        for name in ("q_idx", "q_scale", "k_idx", "k_scale", "w", "q", "latent"):
+            t = d.get(name)
+            setattr(arr[l], name, _ptr(t) if t is not None else None)
+        arr[l].out = _ptr(outs[l])
+    L = lib()
+    need = L.indexcache_forward_ws(roles.encode(), ctypes.byref(shape), ctypes.byref(seqs))
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, dev)
+    stats = Stats()
+    if events is not None:     # ctypes array of hipEvent_t handles created by the caller
+        stats.events = ctypes.cast(events, ctypes.c_void_p)
+        stats.event_cap = len(events)
+    _check(L.indexcache_forward(roles.encode(), arr, ctypes.byref(shape), ctypes.byref(seqs), _ptr(index_cache),
+                                _ptr(score_cache), _ptr(ws), ws.numel() if ws is not None else 0, ctypes.byref(stats),
+                                _stream(stream)))
+    return ForwardResult(outs, index_cache, score_cache, stats)
+
+
+def layer_dict(li) -> dict:
+    """Adapter for objects with q_idx/q_scale/k_idx/k_scale/w/q/latent attributes."""
+    return {n: getattr(li, n) for n in ("q_idx", "q_scale", "k_idx", "k_scale", "w", "q", "latent")}

@@ -1,0 +1,337 @@
+// Lightning-indexer scores into a per-row score slab, then an exact per-row top-k.
+//
+// Score ([IDX] §4, lightning-indexer equation): I[t,s] = sum_j w[t,j] ReLU(q_idx[t,j,:] . k_idx[s,:])
+// over the visible keys s <= t.  Selection ([IDX] §2 TopK; §6.5 deterministic):
+// the k largest scores, ties to the lower position, -0.0 == +0.0.
+//
+// This is the general path (any number of sequences, any query count): it is
+// the decode path (one query per sequence, keys split over many workgroups) and
+// the reference GPU path for prefill.  Per-row work is independent, so the slab
+// is written once and read by the selection kernel.
+//
+// MFMA layout (v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x128_f8f6f4):
+//   rows  (M) = 16 indexer heads of one query, columns (N) = 16 keys,
+//   K = the head dimension.  Lane l supplies head/key (l % 16) and the K slice
+//   selected by (l / 16); the result puts key (l % 16) and heads 4*(l/16)+r in
+//   lane l, so the head-weighted ReLU sum is an in-lane loop plus a reduction
+//   across the four 16-lane groups.
+#include "dsa_device.h"
+#include "launch.h"
+
+namespace dsa {
+
+constexpr int kScoreKeysPerWave = 256;
+
+template <int HB, int D>
+__global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __restrict__ q_idx,
+                                                             const uint16_t* __restrict__ k_idx,
+                                                             const uint16_t* __restrict__ w, int H, dsa_seqs seqs,
+                                                             int64_t n_q, float* __restrict__ slab, int64_t ld) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.y * 4 + wave;
+  if (i >= n_q) return;
+  const int b = seq_of_row(seqs, i);
+  const int64_t p = seqs.q_pos0[b] + (i - seqs.q_start[b]);
+  const int64_t s0 = (int64_t)blockIdx.x * kScoreKeysPerWave;
+  if (s0 > p) return;
+  const int64_t krow0 = seqs.k_start[b];
+  const int c = lane & 15, g = lane >> 4;
+  constexpr int KS = D / 32;
+
+  i32x4 a[HB][KS];
+  float wl[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int head = 16 * hb + c;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (head < H)
+        a[hb][ks] = *reinterpret_cast<const i32x4*>(q_idx + (i * H + head) * D + 32 * ks + 8 * g);
+      else
+        a[hb][ks] = i32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hh = 16 * hb + 4 * g + r;
+      wl[hb][r] = hh < H ? bf16_to_f32(w[i * H + hh]) : 0.f;
+    }
+  }
+
+  for (int sb = 0; sb < kScoreKeysPerWave / 16; ++sb) {
+    const int64_t sbase = s0 + 16 * sb;
+    if (sbase > p) break;
+    const int64_t s = sbase + c;
+    i32x4 bf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (s <= p)
+        bf[ks] = *reinterpret_cast<const i32x4*>(k_idx + (krow0 + s) * D + 32 * ks + 8 * g);
+      else
+        bf[ks] = i32x4{0, 0, 0, 0};
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16_16x16x32(a[hb][ks], bf[ks], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part += wl[hb][r] * fmaxf(acc[r], 0.f);
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (g == 0 && s <= p) slab[i * ld + s] = part;
+  }
+}
+
+// fp8 e4m3: d == 128, one K=128 MFMA per (16 heads x 16 keys).  The positive
+// per-row scales leave the ReLU: w' = w * q_scale folds in before the head sum
+// and k_scale multiplies the finished score.
+template <int HB>
+__global__ __launch_bounds__(256) void idx_score_fp8_kernel(const uint8_t* __restrict__ q_idx,
+                                                            const float* __restrict__ q_scale,
+                                                            const uint8_t* __restrict__ k_idx,
+                                                            const float* __restrict__ k_scale,
+                                                            const uint16_t* __restrict__ w, int H, dsa_seqs seqs,
+                                                            int64_t n_q, float* __restrict__ slab, int64_t ld) {
+  constexpr int D = 128;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.y * 4 + wave;
+  if (i >= n_q) return;
+  const int b = seq_of_row(seqs, i);
+  const int64_t p = seqs.q_pos0[b] + (i - seqs.q_start[b]);
+  const int64_t s0 = (int64_t)blockIdx.x * kScoreKeysPerWave;
+  if (s0 > p) return;
+  const int64_t krow0 = seqs.k_start[b];
+  const int c = lane & 15, g = lane >> 4;
+
+  i32x8 a[HB];
+  float wl[HB][4];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int head = 16 * hb + c;
+    if (head < H) {
+      const i32x4* src = reinterpret_cast<const i32x4*>(q_idx + (i * H + head) * D + 32 * g);
+      i32x4 lo = src[0], hi = src[1];
+      a[hb] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      a[hb] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hh = 16 * hb + 4 * g + r;
+      wl[hb][r] = hh < H ? bf16_to_f32(w[i * H + hh]) * q_scale[i * H + hh] : 0.f;
+    }
+  }
+
+  for (int sb = 0; sb < kScoreKeysPerWave / 16; ++sb) {
+    const int64_t sbase = s0 + 16 * sb;
+    if (sbase > p) break;
+    const int64_t s = sbase + c;
+    i32x8 bf = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    float ks = 0.f;
+    if (s <= p) {
+      const i32x4* src = reinterpret_cast<const i32x4*>(k_idx + (krow0 + s) * D + 32 * g);
+      i32x4 lo = src[0], hi = src[1];
+      bf = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      ks = k_scale[krow0 + s];
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = mfma_fp8_16x16x128(a[hb], bf, acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part += wl[hb][r] * fmaxf(acc[r], 0.f);
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    if (g == 0 && s <= p) slab[i * ld + s] = part * ks;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Exact top-k of one slab row per workgroup (1024 threads).
+//
+// Radix select on the 32-bit order keys, digits of 11, 11 and 10 bits, finds the
+// k-th largest key T and how many keys exceed it; the output pass then walks the
+// row in position order, keeping every key > T and the lowest-position keys == T
+// until k are taken.  Positions therefore come out ascending.
+// ----------------------------------------------------------------------------
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+
+struct SelShared {
+  uint32_t hist[2048];
+  uint32_t wave_tot[kSelWaves];
+  uint32_t wave_tot2[2][kSelWaves];
+  uint32_t digit, above;
+};
+
+// Suffix sums over the histogram: thread t owns bins 2t and 2t+1.
+__device__ void sel_find_digit(SelShared& sh, int nbins, uint32_t remaining) {
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int b0 = 2 * t, b1 = 2 * t + 1;
+  const uint32_t h0 = b0 < nbins ? sh.hist[b0] : 0u;
+  const uint32_t h1 = b1 < nbins ? sh.hist[b1] : 0u;
+  uint32_t v = h0 + h1;
+  // inclusive suffix scan inside the wave (higher lanes own higher bins)
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    uint32_t o = __shfl_down(v, d);
+    if (lane + d < 64) v += o;
+  }
+  if (lane == 0) sh.wave_tot[wv] = v;
+  __syncthreads();
+  uint32_t higher_waves = 0;
+  for (int w2 = wv + 1; w2 < kSelWaves; ++w2) higher_waves += sh.wave_tot[w2];
+  const uint32_t incl = v + higher_waves;            // sum of bins >= b0
+  const uint32_t above1 = incl - (h0 + h1);          // sum of bins > b1
+  if (above1 < remaining && remaining <= above1 + h1) {
+    sh.digit = b1;
+    sh.above = above1;
+  } else if (above1 + h1 < remaining && remaining <= incl) {
+    sh.digit = b0;
+    sh.above = above1 + h1;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* __restrict__ slab, int64_t ld,
+                                                                  dsa_seqs seqs, int64_t n_q, int k,
+                                                                  int32_t* __restrict__ idx_out,
+                                                                  float* __restrict__ score_out) {
+  __shared__ SelShared sh;
+  const int64_t i = blockIdx.x;
+  if (i >= n_q) return;
+  const int b = seq_of_row(seqs, i);
+  const int64_t n = seqs.q_pos0[b] + (i - seqs.q_start[b]) + 1;
+  const float* row = slab + i * ld;
+  int32_t* orow = idx_out + i * (int64_t)k;
+  float* srow = score_out ? score_out + i * (int64_t)k : nullptr;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+
+  if (n <= k) {
+    for (int64_t j = t; j < k; j += kSelThreads) {
+      orow[j] = j < n ? (int32_t)j : -1;
+      if (srow) srow[j] = j < n ? row[j] : 0.f;
+    }
+    return;
+  }
+
+  uint32_t prefix = 0, pmask = 0, remaining = (uint32_t)k;
+  const int shifts[3] = {21, 10, 0};
+  const int widths[3] = {11, 11, 10};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int nb = 1 << widths[pass];
+    const uint32_t dmask = (uint32_t)(nb - 1);
+    for (int j = t; j < 2048; j += kSelThreads) sh.hist[j] = 0u;
+    __syncthreads();
+    for (int64_t s = t; s < n; s += kSelThreads) {
+      const uint32_t key = order_key(row[s]);
+      if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shifts[pass]) & dmask], 1u);
+    }
+    __syncthreads();
+    sel_find_digit(sh, nb, remaining);
+    prefix |= sh.digit << shifts[pass];
+    pmask |= dmask << shifts[pass];
+    remaining -= sh.above;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const uint32_t need_eq = remaining;  // how many keys equal to T are taken (lowest positions)
+
+  uint32_t eq_before = 0, sel_before = 0;
+  int parity = 0;
+  for (int64_t base = 0; base < n; base += kSelThreads, parity ^= 1) {
+    const int64_t s = base + t;
+    const float v = s < n ? row[s] : 0.f;
+    const uint32_t key = s < n ? order_key(v) : 0u;
+    const bool gt = s < n && key > T;
+    const bool eq = s < n && key == T;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const uint64_t eq_ball = __ballot(eq);
+    if (lane == 0) sh.wave_tot[wv] = __popcll(eq_ball);
+    __syncthreads();
+    uint32_t eq_wave_before = 0, eq_total = 0;
+    for (int w2 = 0; w2 < kSelWaves; ++w2) {
+      const uint32_t c2 = sh.wave_tot[w2];
+      if (w2 < wv) eq_wave_before += c2;
+      eq_total += c2;
+    }
+    const uint32_t eq_rank = eq_before + eq_wave_before + (uint32_t)__popcll(eq_ball & lt_mask);
+    const bool sel = gt || (eq && eq_rank < need_eq);
+    const uint64_t sel_ball = __ballot(sel);
+    if (lane == 0) sh.wave_tot2[parity][wv] = __popcll(sel_ball);
+    __syncthreads();
+    uint32_t sel_wave_before = 0, sel_total = 0;
+    for (int w2 = 0; w2 < kSelWaves; ++w2) {
+      const uint32_t c2 = sh.wave_tot2[parity][w2];
+      if (w2 < wv) sel_wave_before += c2;
+      sel_total += c2;
+    }
+    if (sel) {
+      const uint32_t pos = sel_before + sel_wave_before + (uint32_t)__popcll(sel_ball & lt_mask);
+      if (pos < (uint32_t)k) orow[pos] = (int32_t)s;
+      if (srow && pos < (uint32_t)k) srow[pos] = v;
+    }
+    eq_before += eq_total;
+    sel_before += sel_total;
+    if (sel_before >= (uint32_t)k) break;  // uniform: every thread sees the same totals
+  }
+}
+
+// ----------------------------------------------------------------------------
+// launchers
+// ----------------------------------------------------------------------------
+int64_t slab_ld(const dsa_seqs& s) {
+  int64_t mx = 1;
+  for (int b = 0; b < s.B; ++b) {
+    const int64_t nq = s.q_start[b + 1] - s.q_start[b];
+    if (nq > 0) mx = mx > s.q_pos0[b] + nq ? mx : s.q_pos0[b] + nq;
+  }
+  return (mx + 3) & ~int64_t(3);
+}
+
+hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st) {
+  const int64_t n_q = a.seqs.q_start[a.seqs.B];
+  if (n_q == 0) return hipSuccess;
+  const int64_t ld = slab_ld(a.seqs);
+  dim3 grid((unsigned)((ld + kScoreKeysPerWave - 1) / kScoreKeysPerWave), (unsigned)((n_q + 3) / 4));
+  const int HB = (a.H + 15) / 16;
+  if (a.qk_dtype == DSA_BF16) {
+    const uint16_t* q = (const uint16_t*)a.q_idx;
+    const uint16_t* kk = (const uint16_t*)a.k_idx;
+#define DSA_SCORE_BF16(HBv, Dv)                                                                        \
+  if (HB == HBv && a.d == Dv) {                                                                      \
+    hipLaunchKernelGGL((idx_score_bf16_kernel<HBv, Dv>), grid, dim3(256), 0, st, q, kk, a.w, a.H, a.seqs, \
+                       n_q, slab, ld);                                                               \
+    return hipGetLastError();                                                                        \
+  }
+    DSA_SCORE_BF16(1, 64) DSA_SCORE_BF16(1, 128) DSA_SCORE_BF16(2, 64) DSA_SCORE_BF16(2, 128)
+    DSA_SCORE_BF16(4, 64) DSA_SCORE_BF16(4, 128)
+#undef DSA_SCORE_BF16
+  } else {
+    const uint8_t* q = (const uint8_t*)a.q_idx;
+    const uint8_t* kk = (const uint8_t*)a.k_idx;
+#define DSA_SCORE_FP8(HBv)                                                                                 \
+  if (HB == HBv && a.d == 128) {                                                                         \
+    hipLaunchKernelGGL((idx_score_fp8_kernel<HBv>), grid, dim3(256), 0, st, q, a.q_scale, kk, a.k_scale, a.w, \
+                       a.H, a.seqs, n_q, slab, ld);                                                      \
+    return hipGetLastError();                                                                            \
+  }
+    DSA_SCORE_FP8(1) DSA_SCORE_FP8(2) DSA_SCORE_FP8(4)
+#undef DSA_SCORE_FP8
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_topk_select(const IndexerArgs& a, const float* slab, hipStream_t st) {
+  const int64_t n_q = a.seqs.q_start[a.seqs.B];
+  if (n_q == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)n_q), dim3(kSelThreads), 0, st, slab, slab_ld(a.seqs),
+                     a.seqs, n_q, a.k, a.idx_out, a.score_out);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,44 @@
+// Internal launcher interface between the C-ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+struct IndexerArgs {
+  const void* q_idx;
+  const float* q_scale;
+  const void* k_idx;
+  const float* k_scale;
+  const uint16_t* w;
+  int qk_dtype, H, d, k;
+  dsa_seqs seqs;
+  int32_t* idx_out;
+  float* score_out;
+};
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* latent;
+  const int32_t* idx;
+  int n_h, d_qk, d_v, k;
+  float scale;
+  dsa_seqs seqs;
+  void* out;
+  int out_dtype;
+};
+
+// indexer_slab.hip: scores of every visible (row, key) into a [n_q, ld] fp32 slab, then top-k.
+int64_t slab_ld(const dsa_seqs& s);
+hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st);
+hipError_t launch_topk_select(const IndexerArgs& a, const float* slab, hipStream_t st);
+
+// sparse_attn.hip
+int attn_splits(const AttnArgs& a);
+size_t attn_ws_bytes(const AttnArgs& a);
+hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st);
+
+}  // namespace dsa

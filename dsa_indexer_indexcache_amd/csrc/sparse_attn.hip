@@ -1,0 +1,308 @@
+// Sparse MLA attention over the selected latent rows.
+//
+// [IDX] §2: alpha_hat = softmax over S_t only, o_t = sum alpha_hat v_s; §4: DSA reads
+// only the MLA latent rows c_s, s in S_t, and each latent row is shared by every
+// query head (MQA), so one gathered row serves all n_h heads of the query.
+// Here key = c[s, :576], value = c[s, :512], and the score is scale * q . key.
+//
+// One workgroup per query row (prefill) or per (row, split of the index list)
+// (decode, followed by a combine kernel).  Each wave owns 16*HG heads (HG = 1).
+// Per block of 32 selected rows:
+//   gather  : 32 latent rows -> LDS, row-major (keys for QK) and transposed
+//             (first 512 columns, values for PV), invalid slots read as zeros;
+//   QK      : S^T[key][head] = K . Q^T with v_mfma_f32_16x16x32_bf16, A = K rows
+//             from LDS, B = the wave's Q slice held in registers for the whole row;
+//             the output puts one head per lane, keys in registers;
+//   softmax : online, in the exp2 domain; the running max is only raised when a
+//             block exceeds it by more than 2^8 (bounded growth of p), so O is
+//             rescaled rarely; p is rounded to bf16 once and both O and the
+//             normaliser use the rounded value;
+//   PV      : O[head][v] += P . V with P (bf16) as the A operand straight from the
+//             QK registers and V^T rows from LDS as the B operand; the key order
+//             inside the MFMA's K slots is the same permutation for both operands.
+#include "dsa_device.h"
+#include "launch.h"
+
+namespace dsa {
+
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kBlk = 32;                 // selected rows per block
+constexpr int kKsStride = kDqk + 8;      // bf16 elements per LDS key row (pad: conflict-free b128 reads)
+constexpr int kVtStride = kBlk + 4;      // bf16 elements per LDS V^T row
+constexpr float kLazy = 8.0f;            // log2-domain slack before the running max moves
+
+struct AttnSmem {
+  uint16_t ks[kBlk * kKsStride];
+  uint16_t vt[kDv * kVtStride];
+  int valid[kBlk];
+};
+
+template <int HG>
+__global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ latent,
+                                                          const int32_t* __restrict__ idx, int n_h, int k,
+                                                          float scale_log2, dsa_seqs seqs, int64_t n_q, int splits,
+                                                          float* __restrict__ out_f32, uint16_t* __restrict__ out_bf16,
+                                                          float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ AttnSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nthreads = blockDim.x;
+  const int64_t i = blockIdx.x / splits;
+  const int split = blockIdx.x % splits;
+  if (i >= n_q) return;
+  const int b = seq_of_row(seqs, i);
+  const int64_t p = seqs.q_pos0[b] + (i - seqs.q_start[b]);
+  const int64_t krow0 = seqs.k_start[b];
+  const int c = lane & 15, g = lane >> 4;
+  const int head0 = 16 * HG * wave;
+
+  const int nblk_total = (k + kBlk - 1) / kBlk;
+  const int per = (nblk_total + splits - 1) / splits;
+  const int blk_lo = split * per;
+  const int blk_hi = min(nblk_total, blk_lo + per);
+
+  // Q slice: B operand of the QK MFMA, lane -> head (16hg + c), K slice 8g within each 32-column step.
+  i32x4 qf[HG][kDqk / 32];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    const uint16_t* qrow = q + (i * n_h + head0 + 16 * hg + c) * kDqk + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) qf[hg][ks] = *reinterpret_cast<const i32x4*>(qrow + 32 * ks);
+  }
+
+  f32x4 o[HG][kDv / 16];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+    for (int vt = 0; vt < kDv / 16; ++vt) o[hg][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[HG], l[HG];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    m[hg] = -INFINITY;
+    l[hg] = 0.f;
+  }
+
+  const int32_t* irow = idx + i * (int64_t)k;
+  for (int blk = blk_lo; blk < blk_hi; ++blk) {
+    // ---- gather 32 latent rows (row pairs so V^T can be written as packed pairs)
+    for (int task = tid; task < (kBlk / 2) * (kDqk / 8); task += nthreads) {
+      const int rp = task / (kDqk / 8), ch = task % (kDqk / 8);
+      i32x4 v[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int slot = blk * kBlk + 2 * rp + e;
+        const int32_t s = slot < k ? irow[slot] : -1;
+        const bool ok = s >= 0 && s <= p;
+        if (ch == 0) sm.valid[2 * rp + e] = ok;
+        v[e] = ok ? *reinterpret_cast<const i32x4*>(latent + (krow0 + s) * kDqk + 8 * ch) : i32x4{0, 0, 0, 0};
+        *reinterpret_cast<i32x4*>(&sm.ks[(2 * rp + e) * kKsStride + 8 * ch]) = v[e];
+      }
+      if (ch < kDv / 8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t x0 = (uint32_t)v[0][e], x1 = (uint32_t)v[1][e];
+          // columns 8ch+2e and 8ch+2e+1 of rows 2rp and 2rp+1
+          *reinterpret_cast<uint32_t*>(&sm.vt[(8 * ch + 2 * e) * kVtStride + 2 * rp]) = (x0 & 0xFFFFu) | (x1 << 16);
+          *reinterpret_cast<uint32_t*>(&sm.vt[(8 * ch + 2 * e + 1) * kVtStride + 2 * rp]) = (x0 >> 16) | (x1 & 0xFFFF0000u);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for two 16-key tiles
+    f32x4 st[HG][2];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) st[hg][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const i32x4 kf = *reinterpret_cast<const i32x4*>(&sm.ks[(16 * kt + c) * kKsStride + 32 * ks + 8 * g]);
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) st[hg][kt] = mfma_bf16_16x16x32(kf, qf[hg][ks], st[hg][kt]);
+      }
+    }
+
+    // ---- online softmax; lane holds head (16hg + c), keys 16kt + 4g + r
+    bool okr[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) okr[kt][r] = sm.valid[16 * kt + 4 * g + r] != 0;
+    i32x4 pf[HG];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      float x[2][4];
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[kt][r] = okr[kt][r] ? st[hg][kt][r] * scale_log2 : -INFINITY;
+          bmax = fmaxf(bmax, x[kt][r]);
+        }
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      const bool raise = bmax > m[hg] + kLazy;
+      if (__any(raise)) {
+        const float mnew = fmaxf(m[hg], bmax);
+        const float alpha = (m[hg] == -INFINITY) ? 0.f : exp2f(m[hg] - mnew);
+        m[hg] = mnew;
+        l[hg] *= alpha;
+        // alpha for the O layout: lane holds heads 4g + r
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float ar = __shfl(alpha, 4 * g + r);
+#pragma unroll
+          for (int vt = 0; vt < kDv / 16; ++vt) o[hg][vt][r] *= ar;
+        }
+      }
+      // p enters the PV product as bf16; the normaliser sums the same rounded values,
+      // so the rounding of the weights cancels in O / l (a lone dominant key is exact).
+      uint32_t pb[2][4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pr = (m[hg] == -INFINITY) ? 0.f : exp2f(x[kt][r] - m[hg]);
+          pb[kt][r] = f32_to_bf16_bits(pr);
+          psum += __uint_as_float(pb[kt][r] << 16);
+        }
+      l[hg] += psum;
+      pf[hg] = i32x4{(int)(pb[0][0] | (pb[0][1] << 16)), (int)(pb[0][2] | (pb[0][3] << 16)),
+                     (int)(pb[1][0] | (pb[1][1] << 16)), (int)(pb[1][2] | (pb[1][3] << 16))};
+    }
+
+    // ---- O += P V ; B operand lane -> value column 16vt + c, K slots {4g..4g+3, 16+4g..16+4g+3}
+#pragma unroll
+    for (int vt = 0; vt < kDv / 16; ++vt) {
+      __builtin_amdgcn_sched_barrier(0);
+      const uint16_t* vrow = &sm.vt[(16 * vt + c) * kVtStride];
+      const uint64_t lo = *reinterpret_cast<const uint64_t*>(vrow + 4 * g);
+      const uint64_t hi = *reinterpret_cast<const uint64_t*>(vrow + 16 + 4 * g);
+      const i32x4 vf = i32x4{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) o[hg][vt] = mfma_bf16_16x16x32(pf[hg], vf, o[hg][vt]);
+    }
+    __syncthreads();
+  }
+
+  // ---- finish: per-head sums across the four lane groups
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    float lt = l[hg];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (splits == 1) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ir = __shfl(inv, 4 * g + r);
+        const int64_t orow = (i * n_h + head0 + 16 * hg + 4 * g + r) * kDv;
+#pragma unroll
+        for (int vt = 0; vt < kDv / 16; ++vt) {
+          const float val = o[hg][vt][r] * ir;
+          if (out_f32)
+            out_f32[orow + 16 * vt + c] = val;
+          else
+            out_bf16[orow + 16 * vt + c] = (uint16_t)f32_to_bf16_bits(val);
+        }
+      }
+    } else {
+      const int64_t pbase = (i * splits + split) * (int64_t)n_h;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t orow = (pbase + head0 + 16 * hg + 4 * g + r) * kDv;
+#pragma unroll
+        for (int vt = 0; vt < kDv / 16; ++vt) part_o[orow + 16 * vt + c] = o[hg][vt][r];
+      }
+      if (g == 0) {
+        part_ml[(pbase + head0 + 16 * hg + c) * 2 + 0] = m[hg];
+        part_ml[(pbase + head0 + 16 * hg + c) * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
+// Merge split partials: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L.
+__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_ml, int n_h,
+                                                                  int splits, int64_t n_q, float* __restrict__ out_f32,
+                                                                  uint16_t* __restrict__ out_bf16) {
+  const int64_t rh = blockIdx.x;  // (row, head)
+  const int64_t i = rh / n_h;
+  const int h = (int)(rh % n_h);
+  if (i >= n_q) return;
+  float M = -INFINITY;
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((i * splits + s) * n_h + h) * 2]);
+  float L = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float ms = part_ml[((i * splits + s) * n_h + h) * 2];
+    if (ms != -INFINITY) L += part_ml[((i * splits + s) * n_h + h) * 2 + 1] * exp2f(ms - M);
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  for (int v = threadIdx.x; v < kDv; v += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < splits; ++s) {
+      const float ms = part_ml[((i * splits + s) * n_h + h) * 2];
+      if (ms != -INFINITY) acc += part_o[((i * splits + s) * n_h + h) * kDv + v] * exp2f(ms - M);
+    }
+    const float val = acc * inv;
+    if (out_f32)
+      out_f32[(i * n_h + h) * kDv + v] = val;
+    else
+      out_bf16[(i * n_h + h) * kDv + v] = (uint16_t)f32_to_bf16_bits(val);
+  }
+}
+
+int attn_splits(const AttnArgs& a) {
+  const int64_t n_q = a.seqs.q_start[a.seqs.B];
+  const int nblk = (a.k + kBlk - 1) / kBlk;
+  if (n_q >= 512 || nblk <= 1) return 1;
+  // spread few rows over enough workgroups to fill 256 CUs
+  int s = (int)((1024 + n_q - 1) / n_q);
+  if (s > nblk) s = nblk;
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : s;
+}
+
+size_t attn_ws_bytes(const AttnArgs& a) {
+  const int s = attn_splits(a);
+  if (s == 1) return 0;
+  const int64_t n_q = a.seqs.q_start[a.seqs.B];
+  return (size_t)n_q * s * a.n_h * (kDv + 2) * sizeof(float) + 256;
+}
+
+hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
+  const int64_t n_q = a.seqs.q_start[a.seqs.B];
+  if (n_q == 0) return hipSuccess;
+  const int splits = attn_splits(a);
+  const float scale_log2 = a.scale * 1.4426950408889634f;
+  float* out_f32 = a.out_dtype == DSA_FP32 ? (float*)a.out : nullptr;
+  uint16_t* out_bf16 = a.out_dtype == DSA_BF16 ? (uint16_t*)a.out : nullptr;
+  float* part_o = nullptr;
+  float* part_ml = nullptr;
+  if (splits > 1) {
+    part_o = (float*)ws;
+    part_ml = part_o + (size_t)n_q * splits * a.n_h * kDv;
+  }
+  // 16 heads per wave: the Q slice (72 VGPRs) and the O accumulator (128) stay
+  // resident with two waves per SIMD and no spills.
+  const int waves = a.n_h / 16;
+  dim3 grid((unsigned)(n_q * splits));
+  hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(64 * waves), 0, st, a.q, a.latent, a.idx, a.n_h, a.k,
+                     scale_log2, a.seqs, n_q, splits, splits == 1 ? out_f32 : nullptr,
+                     splits == 1 ? out_bf16 : nullptr, part_o, part_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3((unsigned)(n_q * a.n_h)), dim3(256), 0, st, part_o, part_ml,
+                     a.n_h, splits, n_q, out_f32, out_bf16);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

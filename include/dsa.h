@@ -1,0 +1,213 @@
+/*
+ * dsa.h — C ABI of the MI355X (gfx950) DSA hot path: lightning indexer, per-query
+ * top-k, sparse MLA attention, and the IndexCache F/S layer loop.
+ *
+ * Sources (page titles; sections/equations named at each declaration):
+ *   [IDX] Jerry's Blog, "注意力机制中的 Index：从位置下标到预算检索"
+ *   [IC]  "读懂 IndexCache：从 DSA 的选词开销到跨层索引复用"
+ *
+ * Conventions shared by every entry point
+ *   - Device pointers are HIP device addresses; host pointers are marked (host).
+ *   - All tensors are dense, row-major, with 16-byte aligned base pointers.
+ *   - bf16 tensors are passed as uint16_t bit patterns; fp8 tensors are OCP
+ *     e4m3fn bytes (max 448) with one positive fp32 scale per row.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are enqueued
+ *     asynchronously on it; the library never synchronises, never allocates
+ *     device memory and keeps no pointer after it returns.  Device-side faults
+ *     surface at the caller's next synchronisation.
+ *   - The caller owns every buffer, including the workspace `ws`, whose size is
+ *     given by the matching *_ws() query.  Outputs must not alias inputs.
+ *   - Validation happens before any launch: on a non-zero status nothing has
+ *     been enqueued and outputs are untouched.  No C++ exception crosses the ABI.
+ *   - Reentrant: the only global state is per-device properties initialised once
+ *     under a lock.
+ */
+#ifndef DSA_MI355X_H
+#define DSA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- status */
+enum {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = -1, /* null required pointer, k < 1, bad sizes, bad sequence table */
+  DSA_ERR_ROLES = -2,       /* empty role string or a character outside {F,S}            */
+  DSA_ERR_FIRST_NOT_F = -3, /* roles[0] != 'F': S layers would have no indices ([IC] §1.1) */
+  DSA_ERR_UNSUPPORTED = -4, /* (H, d, n_h, d_qk, d_v, dtype) combination not compiled       */
+  DSA_ERR_ALIGNMENT = -5,   /* a base pointer is not 16-byte aligned                         */
+  DSA_ERR_WORKSPACE = -6,   /* ws_bytes smaller than the *_ws() query                        */
+  DSA_ERR_HIP = -7          /* a HIP launch failed (detail in dsa_last_error())             */
+};
+
+typedef enum {
+  DSA_BF16 = 0,     /* uint16 bf16 bit patterns                     */
+  DSA_FP8_E4M3 = 1, /* OCP e4m3fn bytes + fp32 per-row scales       */
+  DSA_FP32 = 2
+} dsa_dtype;
+
+#define DSA_MAX_B 64        /* sequences per call                  */
+#define DSA_MAX_LAYERS 256  /* layers per indexcache_forward call  */
+
+/*
+ * Packed variable-length batch (host struct, passed to kernels by value).
+ * Sequence b owns query rows [q_start[b], q_start[b+1]) and key/latent rows
+ * [k_start[b], k_start[b+1]).  Query row i of sequence b sits at absolute
+ * position p = q_pos0[b] + (i - q_start[b]) and sees the key rows
+ * k_start[b] .. k_start[b] + p inclusive (visible set s <= t, [IDX] §4 memory
+ * M_t = {c_s : s <= t}); p must be < k_start[b+1] - k_start[b].
+ * Positions written to index outputs are sequence-local (0..p).
+ *   prefill chunk: B = 1, q_pos0[0] = position of the chunk's first query;
+ *   decode step:   q_start = {0,1,..,B}, q_pos0[b] = len_b - 1 (the new token
+ *                  is already in the caches).
+ */
+typedef struct {
+  int32_t B;
+  int32_t reserved;
+  int64_t q_start[DSA_MAX_B + 1];
+  int64_t k_start[DSA_MAX_B + 1];
+  int64_t q_pos0[DSA_MAX_B];
+} dsa_seqs;
+
+/* ---------------------------------------------------------------- indexer + top-k */
+/*
+ * Lightning indexer score and per-query top-k ([IDX] §4 score equation
+ * I[t,s] = sum_j w[t,j] ReLU(q_idx[t,j,:] . k_idx[s,:]); §2 S_t = TopK_k over the
+ * visible set; §6.5 the selection must be deterministic).
+ *
+ *   q_idx   [n_q, H, d]  bf16 or e4m3fn         (device)
+ *   q_scale [n_q, H]     fp32 > 0, fp8 only     (device, NULL for bf16)
+ *   k_idx   [n_k, d]     bf16 or e4m3fn         (device)
+ *   k_scale [n_k]        fp32 > 0, fp8 only     (device, NULL for bf16)
+ *   w       [n_q, H]     bf16                   (device)
+ *   idx_out [n_q, k]     int32                  (device, written)
+ *   score_out [n_q, k]   fp32, optional         (device, written; NULL to skip)
+ * For fp8 the dequantised values are scale * code; the score equals the
+ * definition applied to them (the positive scales are folded out of the ReLU).
+ * Row i receives exactly min(k, p+1) distinct positions in [0, p], ranked by
+ * score descending then position ascending (ties go to the lower position;
+ * -0.0 == +0.0); the remaining slots are -1.  Valid positions are written in
+ * ascending order.  score_out[i, j] is the fp32 score of idx_out[i, j] (0 for
+ * -1 slots).  Scores are computed in fp32 from exact input products.
+ * Supported: H in {8,16,32,64} (rounded up to 16 internally), d in {64,128};
+ * fp8 needs d == 128.  Returns DSA_ERR_UNSUPPORTED otherwise.
+ */
+int dsa_indexer_topk(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
+                     const uint16_t* w, int qk_dtype, int H, int d, int k, const dsa_seqs* seqs /* host */,
+                     int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes dsa_indexer_topk needs for this shape (0 is possible). */
+size_t dsa_indexer_topk_ws(int qk_dtype, int H, int d, int k, const dsa_seqs* seqs /* host */);
+
+/* ---------------------------------------------------------------- sparse attention */
+/*
+ * Sparse MLA attention over the selected latent rows ([IDX] §2 sparse softmax
+ * over S_t and o_t = sum alpha_hat v_s; §4 the latent row c_s is shared by all
+ * query heads):
+ *   out[i,h,:] = sum_{s in S_i} softmax_s(scale * q[i,h,:d_qk] . c[s,:d_qk]) * c[s,:d_v]
+ *
+ *   q      [n_q, n_h, d_qk] bf16   (device)
+ *   latent [n_k, d_qk]      bf16   (device; keys = all d_qk columns, values = first d_v)
+ *   idx    [n_q, k]         int32  (device; sequence-local positions, -1 = unused slot;
+ *                                   entries outside [0, p] are skipped, never read)
+ *   out    [n_q, n_h, d_v]  fp32 or bf16 (out_dtype)  (device, written)
+ * A row with no usable index gets out = 0.  Softmax and accumulation are fp32.
+ * Supported: n_h in {16,32,64,128}, d_qk == 576, d_v == 512.
+ */
+int dsa_sparse_attn(const uint16_t* q, const uint16_t* latent, const int32_t* idx, int n_h, int d_qk, int d_v,
+                    int k, float scale, const dsa_seqs* seqs /* host */, void* out, int out_dtype, void* ws,
+                    size_t ws_bytes, void* stream);
+
+size_t dsa_sparse_attn_ws(int n_h, int d_qk, int d_v, int k, const dsa_seqs* seqs /* host */);
+
+/* ---------------------------------------------------------------- IndexCache */
+/* One layer's tensors (device pointers).  q_idx/q_scale/k_idx/k_scale/w are read
+ * only when the layer's role is F. */
+typedef struct {
+  const void* q_idx;
+  const float* q_scale;
+  const void* k_idx;
+  const float* k_scale;
+  const uint16_t* w;
+  const uint16_t* q;
+  const uint16_t* latent;
+  void* out;
+} dsa_layer;
+
+typedef struct {
+  int32_t H, d, k;          /* indexer heads, head dim, top-k budget   */
+  int32_t n_h, d_qk, d_v;   /* attention heads, latent width, value width */
+  float scale;              /* softmax scale (1/sqrt(d_qk) for MLA)     */
+  int32_t qk_dtype;         /* dsa_dtype of q_idx/k_idx                 */
+  int32_t out_dtype;        /* dsa_dtype of out (DSA_FP32 or DSA_BF16)  */
+  int32_t reserved;
+  int64_t q_chunk;          /* query rows per chunk (>= 1)               */
+  int64_t index_rows;       /* rows of index_cache / score_cache         */
+  int64_t out_rows;         /* rows of every layer's out buffer           */
+} dsa_shape;
+
+#define DSA_MAX_TRACE 1024 /* traced calls per indexcache_forward call */
+
+typedef struct {
+  /* in (optional): launch tracing.  events points to caller-created hipEvent_t
+   * handles (host array of event_cap entries, may be NULL).  Call j of the loop
+   * (one dsa_indexer_topk or dsa_sparse_attn step) is bracketed by
+   * hipEventRecord(events[2j]) and hipEventRecord(events[2j+1]) on the stream;
+   * the library records only and never synchronises or queries them. */
+  void** events;
+  int32_t event_cap;
+  /* out */
+  int32_t n_layers;
+  int32_t n_indexer_calls;          /* = number of F layers (the indexer work kept)  */
+  int32_t n_chunks;
+  int32_t n_traced;                 /* event pairs recorded                           */
+  int32_t reserved;
+  int32_t src_layer[DSA_MAX_LAYERS]; /* layer whose indices layer l attends with      */
+  int8_t trace_kind[DSA_MAX_TRACE];  /* 0 = indexer + top-k, 1 = sparse attention      */
+  int16_t trace_layer[DSA_MAX_TRACE];
+  int32_t trace_chunk[DSA_MAX_TRACE];
+} dsa_stats;
+
+/*
+ * Index-reuse inference loop ([IC] §1.1 F/S roles; §1.2 the loop that keeps one
+ * index tensor, overwritten by each F layer and read by every later S layer).
+ * roles: NUL-terminated (host), one 'F' or 'S' per layer; n_layers = strlen(roles).
+ * For each chunk of shape->q_chunk query rows (chunked prefill order: every
+ * layer of chunk c before chunk c+1), for each layer l:
+ *   role F: dsa_indexer_topk on layer l's indexer tensors -> index_cache
+ *   every layer: dsa_sparse_attn(layer l's q and latent, index_cache) -> layer l's out
+ * An S layer therefore attends over the positions chosen by the nearest
+ * preceding F layer, with its own q and latent.  Row i of the index cache lives
+ * in slot (i mod index_rows) and row i of out in slot (i mod out_rows); each of
+ * index_rows / out_rows must be >= n_q, or a multiple of q_chunk (a ring that
+ * holds the current chunk).  score_cache (optional) mirrors index_cache.
+ * stats (host, optional) receives the plan and call count, and optionally
+ * brackets each step with caller-provided events (see dsa_stats).
+ */
+int indexcache_forward(const char* roles, const dsa_layer* layers /* host array */, const dsa_shape* shape /* host */,
+                       const dsa_seqs* seqs /* host */, int32_t* index_cache, float* score_cache, void* ws,
+                       size_t ws_bytes, dsa_stats* stats /* host */, void* stream);
+
+size_t indexcache_forward_ws(const char* roles, const dsa_shape* shape, const dsa_seqs* seqs);
+
+/*
+ * Host-only planning of the loop above ([IC] §1.1: the first layer must be F;
+ * an S layer uses the nearest preceding F layer).  src_layer (host, n_layers
+ * entries, may be NULL) receives max{l' <= l : roles[l'] == 'F'};
+ * n_indexer_calls (host, may be NULL) the number of F layers.  Needs no GPU.
+ */
+int indexcache_plan(const char* roles, int32_t* src_layer, int32_t* n_indexer_calls);
+
+/* ---------------------------------------------------------------- misc */
+const char* dsa_status_string(int status); /* static string                         */
+const char* dsa_last_error(void);          /* thread-local detail of the last error */
+int dsa_version(void);                     /* ABI version (major*100 + minor)        */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSA_MI355X_H */

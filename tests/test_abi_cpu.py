@@ -1,0 +1,143 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and its
+host-only logic (role planning, argument validation, workspace queries) behaves as
+include/dsa.h states.  No compute entry point reaches a kernel here: every call
+below is rejected by validation before any launch, or is host-only."""
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import oracle
+import dsa_indexer_indexcache_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dsa.LIB_PATH), reason="HIP library not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_][a-z_0-9]*)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(dsa.EXPORTS), names
+    L = dsa.lib()
+    for n in names:
+        assert hasattr(L, n)
+    assert L.dsa_version() == 100
+
+
+def test_status_strings():
+    L = dsa.lib()
+    for code in dsa.STATUS:
+        assert L.dsa_status_string(code)
+    assert L.dsa_status_string(-99) == b"unknown status"
+
+
+def test_plan_matches_oracle_on_random_roles():
+    rnd = random.Random(0)
+    for _ in range(500):
+        n = rnd.randint(1, 60)
+        roles = "F" + "".join(rnd.choice("FS") for _ in range(n - 1))
+        assert dsa.indexcache_plan(roles) == oracle.indexcache_plan(roles)
+    assert dsa.indexcache_plan("FSSSFSSS") == ([0, 0, 0, 0, 4, 4, 4, 4], 2)
+    assert dsa.indexcache_plan("FSSS" * 11 + "FSS")[1] == 12
+
+
+@pytest.mark.parametrize("roles,code", [("", -2), ("FX", -2), ("fS", -2), ("SFFF", -3), ("S", -3)])
+def test_plan_rejects(roles, code):
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.indexcache_plan(roles)
+    assert e.value.status == code
+    with pytest.raises(oracle.RoleError):
+        oracle.indexcache_plan(roles)
+
+
+FAKE = 1 << 40   # never dereferenced: every call below fails validation first
+
+
+def _topk(**kw):
+    a = dict(q_idx=FAKE, q_scale=None, k_idx=FAKE, k_scale=None, w=FAKE, dt=0, H=64, d=128, k=2048,
+             seqs=dsa.Seqs.prefill(100), idx=FAKE, sc=None, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return dsa.lib().dsa_indexer_topk(a["q_idx"], a["q_scale"], a["k_idx"], a["k_scale"], a["w"], a["dt"], a["H"],
+                                      a["d"], a["k"], ctypes.byref(a["seqs"]), a["idx"], a["sc"], a["ws"], a["wsb"],
+                                      None)
+
+
+def test_indexer_validation():
+    assert _topk(k=0) == -1
+    assert _topk(H=65) == -4
+    assert _topk(d=96) == -4
+    assert _topk(dt=1, d=64, q_scale=FAKE, k_scale=FAKE) == -4       # fp8 needs d=128
+    assert _topk(dt=1) == -1                                        # fp8 without scales
+    assert _topk(q_scale=FAKE) == -1                                # bf16 with scales
+    assert _topk(q_idx=FAKE + 8) == -5
+    assert _topk(idx=None) == -1
+    assert _topk(wsb=16) == -6
+    bad = dsa.Seqs.prefill(100, n_k=50)                              # positions beyond the keys
+    assert _topk(seqs=bad) == -1
+    s = dsa.Seqs.prefill(4)
+    s.B = 0
+    assert _topk(seqs=s) == -1
+    assert dsa.lib().dsa_last_error()
+
+
+def _attn(**kw):
+    a = dict(q=FAKE, lat=FAKE, idx=FAKE, n_h=128, dqk=576, dv=512, k=2048, scale=0.04,
+             seqs=dsa.Seqs.prefill(100), out=FAKE, odt=2, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    return dsa.lib().dsa_sparse_attn(a["q"], a["lat"], a["idx"], a["n_h"], a["dqk"], a["dv"], a["k"], a["scale"],
+                                     ctypes.byref(a["seqs"]), a["out"], a["odt"], a["ws"], a["wsb"], None)
+
+
+def test_attention_validation():
+    assert _attn(n_h=48) == -4
+    assert _attn(dqk=512) == -4
+    assert _attn(dv=600) == -1
+    assert _attn(k=0) == -1
+    assert _attn(odt=1) == -4
+    assert _attn(q=None) == -1
+    assert _attn(out=FAKE + 4) == -5
+    dec = dsa.Seqs.decode([100, 200])
+    need = dsa.lib().dsa_sparse_attn_ws(128, 576, 512, 2048, ctypes.byref(dec))
+    assert need > 0                                                # few rows -> split partials
+    assert _attn(seqs=dec, wsb=need - 1) == -6
+
+
+def test_workspace_queries():
+    L = dsa.lib()
+    s = dsa.Seqs.prefill(1000)
+    assert L.dsa_indexer_topk_ws(0, 64, 128, 2048, ctypes.byref(s)) >= 1000 * 1000 * 4
+    assert L.dsa_sparse_attn_ws(128, 576, 512, 2048, ctypes.byref(s)) == 0
+    sh = dsa.Shape(H=64, d=128, k=2048, n_h=128, d_qk=576, d_v=512, scale=0.04, qk_dtype=0, out_dtype=2,
+                   q_chunk=256, index_rows=1000, out_rows=256)
+    assert L.indexcache_forward_ws(b"FSSS", ctypes.byref(sh), ctypes.byref(s)) >= 256 * 1000 * 4
+
+
+def test_forward_validation():
+    L = dsa.lib()
+    s = dsa.Seqs.prefill(64)
+    sh = dsa.Shape(H=64, d=128, k=16, n_h=16, d_qk=576, d_v=512, scale=0.04, qk_dtype=0, out_dtype=2,
+                   q_chunk=32, index_rows=64, out_rows=64)
+    layers = (dsa.Layer * 2)()
+    for l in layers:
+        l.q_idx = l.k_idx = l.w = l.q = l.latent = l.out = FAKE
+    st = dsa.Stats()
+    call = lambda roles, shape=sh, ic=FAKE: L.indexcache_forward(roles, layers, ctypes.byref(shape), ctypes.byref(s),
+                                                                 ic, None, FAKE, 0, ctypes.byref(st), None)
+    assert call(b"SF") == -3
+    assert call(b"FQ") == -2
+    assert call(b"FS", ic=None) == -1
+    bad = dsa.Shape(**{f: getattr(sh, f) for f, _ in dsa.Shape._fields_})
+    bad.out_rows = 48                                              # neither >= n_q nor a multiple of q_chunk
+    assert call(b"FS", shape=bad) == -1
+    bad.out_rows, bad.n_h = 64, 20
+    assert call(b"FS", shape=bad) == -4
+    assert call(b"FS") == -6                                       # workspace 0 bytes

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Small shapes span several key tiles and ragged tails; edge cases cover one-row
+inputs, budgets larger than the prefix, all-equal scores and signed zeros,
+out-of-range index entries, empty batches and the decode (split) attention path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import dsa_indexer_indexcache_amd as dsa
+import oracle
+import synth
+from parity import (ATTN_ATOL, OracleView, check_attention, check_indexer, check_valid_row, row_geometry,
+                    sample_rows)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def announce(msg):
+    print("[case] " + msg, flush=True)
+
+
+def layer(L, H, d, n_h, wid=9, layer_id=0, dtype="bf16", integer=False, n_k=None):
+    li = synth.make_layer(L, L if n_k is None else n_k, H, d, n_h, wid=wid, layer=layer_id, qk_dtype=dtype,
+                          integer_indexer=integer)
+    return li.to(DEV)
+
+
+# --------------------------------------------------------------------------- integer-valued: bit-exact
+
+def test_integer_workload_bit_exact():
+    announce("integer L=1024 H=8 d=64 k=128 n_h=16")
+    li = synth.workload_layer(0, 0).to(DEV)
+    seqs = dsa.Seqs.prefill(1024)
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 128, seqs, want_scores=True)
+    torch.cuda.synchronize()
+    view = OracleView(li)
+    st = check_indexer(view, seqs, range(1024), 128, idx, sc, exact=True)
+    assert st["rows"] == 1024
+    out = dsa.sparse_attn(li.q, li.latent, idx, seqs)
+    torch.cuda.synchronize()
+    check_attention(view, seqs, range(0, 1024, 3), idx, out, synth.WORKLOADS[0].scale)
+
+
+@pytest.mark.parametrize("H,d", [(16, 64), (32, 128), (64, 64)])
+def test_integer_other_head_shapes(H, d):
+    announce("integer H=%d d=%d" % (H, d))
+    li = layer(700, H, d, 16, integer=True)
+    seqs = dsa.Seqs.prefill(700)
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 97, seqs, want_scores=True)
+    torch.cuda.synchronize()
+    check_indexer(OracleView(li), seqs, range(700), 97, idx, sc, exact=True)
+
+
+# --------------------------------------------------------------------------- float inputs
+
+@pytest.mark.parametrize("L,k", [(2500, 256), (2500, 2048), (513, 7)])
+def test_bf16_indexer(L, k):
+    announce("bf16 indexer L=%d k=%d" % (L, k))
+    li = layer(L, 64, 128, 16, wid=1)
+    seqs = dsa.Seqs.prefill(L)
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, seqs, want_scores=True)
+    torch.cuda.synchronize()
+    st = check_indexer(OracleView(li), seqs, sample_rows(L, k, 96), k, idx, sc, exact=False)
+    print(st)
+
+
+def test_fp8_indexer():
+    announce("fp8 indexer L=3000 k=512")
+    li = layer(3000, 64, 128, 16, wid=4, dtype="fp8")
+    seqs = dsa.Seqs.prefill(3000)
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 512, seqs, q_scale=li.q_scale, k_scale=li.k_scale,
+                               want_scores=True)
+    torch.cuda.synchronize()
+    print(check_indexer(OracleView(li), seqs, sample_rows(3000, 512, 96), 512, idx, sc, exact=False))
+
+
+def test_chunk_offsets_match_one_call():
+    """Queries scored in chunks (q_pos0 > 0, full key prefix) give the same rows as one call."""
+    announce("chunked indexer")
+    L, k = 1500, 300
+    li = layer(L, 64, 128, 16, wid=1, layer_id=2)
+    full, fs = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, dsa.Seqs.prefill(L), want_scores=True)
+    parts = []
+    for r0 in range(0, L, 512):
+        r1 = min(L, r0 + 512)
+        s = dsa.Seqs.prefill(r1 - r0, n_k=L, q_pos0=r0)
+        parts.append(dsa.indexer_topk(li.q_idx[r0:r1].contiguous(), li.k_idx, li.w[r0:r1].contiguous(), k, s,
+                                      want_scores=True))
+    torch.cuda.synchronize()
+    assert torch.equal(full, torch.cat([p[0] for p in parts]))
+    assert torch.equal(fs, torch.cat([p[1] for p in parts]))
+
+
+# --------------------------------------------------------------------------- edge cases
+
+def test_ties_and_signed_zero():
+    """All-zero indexer queries: every score is +-0, so the lowest positions win."""
+    announce("ties")
+    L, k = 600, 50
+    li = layer(L, 64, 128, 16, wid=1)
+    qz = torch.zeros_like(li.q_idx)
+    w = li.w.clone()
+    w[:, ::2] = -w[:, ::2].abs()                      # negative weights times ReLU(0) give -0.0 terms
+    idx, sc = dsa.indexer_topk(qz, li.k_idx, w, k, dsa.Seqs.prefill(L), want_scores=True)
+    torch.cuda.synchronize()
+    ig = idx.cpu().numpy()
+    for t in range(L):
+        m = min(k, t + 1)
+        assert ig[t, :m].tolist() == list(range(m)) and np.all(ig[t, m:] == -1)
+    assert torch.all(sc == 0)
+
+
+@pytest.mark.parametrize("L,k", [(1, 1), (1, 5), (17, 1), (64, 64), (65, 64)])
+def test_tiny_inputs(L, k):
+    announce("tiny L=%d k=%d" % (L, k))
+    li = layer(L, 8, 64, 16, integer=True)
+    seqs = dsa.Seqs.prefill(L)
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, seqs, want_scores=True)
+    out = dsa.sparse_attn(li.q, li.latent, idx, seqs)
+    torch.cuda.synchronize()
+    view = OracleView(li)
+    check_indexer(view, seqs, range(L), k, idx, sc, exact=True)
+    check_attention(view, seqs, range(L), idx, out, 576 ** -0.5)
+
+
+def test_empty_batch_is_a_no_op():
+    announce("empty")
+    q = torch.empty((0, 8, 64), dtype=torch.bfloat16, device=DEV)
+    kk = torch.empty((5, 64), dtype=torch.bfloat16, device=DEV)
+    w = torch.empty((0, 8), dtype=torch.bfloat16, device=DEV)
+    idx, _ = dsa.indexer_topk(q, kk, w, 4, dsa.Seqs.prefill(0, n_k=5))
+    assert idx.shape == (0, 4)
+
+
+@pytest.mark.parametrize("n_h", [16, 32, 64, 128])
+def test_attention_random_indices(n_h):
+    """Index rows with -1 padding, duplicates and out-of-range entries (skipped, never read)."""
+    announce("attention n_h=%d" % n_h)
+    L, k = 400, 100
+    li = layer(L, 8, 64, n_h, wid=1)
+    g = np.random.default_rng(n_h)
+    idx = np.full((L, k), -1, np.int32)
+    for t in range(L):
+        m = g.integers(0, k + 1)
+        idx[t, :m] = g.integers(-2, t + 3, size=m)     # includes -2, t+1, t+2: not visible
+    idx_t = torch.from_numpy(idx).to(DEV)
+    seqs = dsa.Seqs.prefill(L)
+    out = dsa.sparse_attn(li.q, li.latent, idx_t, seqs)
+    torch.cuda.synchronize()
+    check_attention(OracleView(li), seqs, range(0, L, 7), idx_t, out, 576 ** -0.5)
+    out_bf = dsa.sparse_attn(li.q, li.latent, idx_t, seqs, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref = out.to(torch.bfloat16)
+    assert (out_bf.float() - ref.float()).abs().max().item() <= 2 ** -7 * max(1.0, out.abs().max().item())
+
+
+# --------------------------------------------------------------------------- decode (varlen, split attention)
+
+def test_decode_varlen():
+    announce("decode varlen")
+    lens = [3000, 5000, 4097, 1]
+    li = synth.make_layer(len(lens), sum(lens), 64, 128, 128, wid=3, layer=7).to(DEV)
+    seqs = dsa.Seqs.decode(lens)
+    k = 2048
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, seqs, want_scores=True)
+    out = dsa.sparse_attn(li.q, li.latent, idx, seqs)
+    torch.cuda.synchronize()
+    view = OracleView(li)
+    check_indexer(view, seqs, range(len(lens)), k, idx, sc, exact=False)
+    check_attention(view, seqs, range(len(lens)), idx, out, 576 ** -0.5)
+
+
+# --------------------------------------------------------------------------- IndexCache loop
+
+def _stack(roles, L, k, wid=2, chunk=None, n_h=16):
+    layers = [synth.make_layer(L, L, 64, 128, n_h, wid=wid, layer=l).to(DEV) for l in range(len(roles))]
+    res = dsa.indexcache_forward(roles, [dsa.layer_dict(x) for x in layers], k, q_chunk=chunk)
+    torch.cuda.synchronize()
+    return layers, res
+
+
+def test_indexcache_fsss_against_oracle():
+    announce("FSSSFSSS")
+    L, k = 600, 64
+    layers, res = _stack("FSSSFSSS", L, k)
+    assert res.n_indexer_calls == 2 and res.src_layer == [0, 0, 0, 0, 4, 4, 4, 4]
+    rows = sample_rows(L, k, 24)
+    seqs = dsa.Seqs.prefill(L)
+    # the cache after the loop holds layer 5's selection (the last F layer)
+    check_indexer(OracleView(layers[4]), seqs, rows, k, res.index_cache, None, exact=False)
+    # every layer attends with its own q/latent over its F layer's rows
+    idx_f = {}
+    for f in (0, 4):
+        idx_f[f], _ = dsa.indexer_topk(layers[f].q_idx, layers[f].k_idx, layers[f].w, k, seqs)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_f[4], res.index_cache)
+    for l in range(8):
+        src = res.src_layer[l]
+        check_attention(OracleView(layers[l]), seqs, rows, idx_f[src], res.outs[l], 576 ** -0.5)
+        if l not in (0, 4):
+            own = dsa.sparse_attn(layers[l].q, layers[l].latent, idx_f[src], seqs)
+            torch.cuda.synchronize()
+            assert torch.equal(own, res.outs[l])
+
+
+def test_all_f_runs_every_indexer_and_chunking_is_invisible():
+    announce("FFFF / chunks")
+    L, k = 700, 100
+    layers, a = _stack("FFFF", L, k)
+    assert a.n_indexer_calls == 4
+    _, b = _stack("FFFF", L, k, chunk=256)
+    assert b.n_chunks == 3
+    assert torch.equal(a.index_cache, b.index_cache)
+    # 256-row chunks take the split-combine attention path: P is rounded to bf16 against a
+    # different running max there, so the two agree to bf16 resolution (both are checked
+    # against the oracle elsewhere)
+    for l in range(4):
+        assert torch.allclose(a.outs[l], b.outs[l], rtol=0, atol=5e-3)
+    # ring-buffered outputs hold the last chunk
+    res = dsa.indexcache_forward("FS", [dsa.layer_dict(x) for x in layers[:2]], k, q_chunk=256, out_rows=256,
+                                 index_rows=256)
+    torch.cuda.synchronize()
+    last = slice(512, 700)
+    full = dsa.indexcache_forward("FS", [dsa.layer_dict(x) for x in layers[:2]], k)
+    torch.cuda.synchronize()
+    assert torch.allclose(res.outs[1][: 700 - 512], full.outs[1][last], rtol=0, atol=5e-3)
+    assert torch.equal(res.index_cache[: 700 - 512], full.index_cache[last])
