@@ -229,6 +229,249 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
   }
 }
 
+// ----------------------------------------------------------------------------
+// Paired-wave variant (n_h a multiple of 32, k <= kIdxMax).
+//
+// A pair of waves owns 16*HG heads.  QK is split over the 576 latent columns
+// (wave vh takes columns [288 vh, 288 vh + 288)), so each wave keeps only half of
+// its heads' q in registers; the two partial score tiles are summed through LDS,
+// after which both waves hold identical scores and run the same softmax.  PV is
+// split over the value columns (wave vh accumulates columns [256 vh, 256 vh + 256)),
+// so each wave's O accumulator is 16*HG x 256.
+// Latent rows are gathered with direct global->LDS loads (no registers), one
+// block ahead of the block being computed, into a row-major tile padded to 73
+// granules per row (conflict-free b128 reads across 16 rows); V is read back
+// column-wise with the LDS transpose read, so no transposed copy is written.
+// ----------------------------------------------------------------------------
+constexpr int kGran = kDqk / 8 + 1;               // 16-byte granules per LDS row (72 + 1 pad)
+constexpr int kRowBytes = kGran * 16;             // 1168: rows land on distinct banks
+constexpr int kTileIns = (kBlk * kGran + 63) / 64;  // 64-lane x 16-byte loads per block (37)
+constexpr int kTileBytes = kTileIns * 1024;       // the last load spills into the tail pad
+constexpr int kNBuf = 2;
+constexpr int kIdxMax = 2048;
+constexpr int kMaxWaves = 8;
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef v4i16 __attribute__((address_space(3))) lds_v4i16;
+
+struct PairSmem {
+  uint8_t tile[kNBuf][kTileBytes];
+  f32x4 xs[kMaxWaves][4][64];   // partial score exchange, [wave][register quad][lane]
+  int idx[kIdxMax];             // the row's selected positions (-1 = skip)
+};
+
+__device__ __forceinline__ uint32_t tile_off(int row, int chunk) { return (uint32_t)(row * kRowBytes + 16 * chunk); }
+
+template <int HG>
+__global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ latent,
+                                                               const int32_t* __restrict__ idx, int n_h, int k,
+                                                               float scale_log2, dsa_seqs seqs, int64_t n_q, int splits,
+                                                               float* __restrict__ out_f32,
+                                                               uint16_t* __restrict__ out_bf16,
+                                                               float* __restrict__ part_o, float* __restrict__ part_ml) {
+  __shared__ PairSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int pair = wave >> 1, vh = wave & 1;
+  const int64_t i = blockIdx.x / splits;
+  const int split = blockIdx.x % splits;
+  if (i >= n_q) return;
+  const int b = seq_of_row(seqs, i);
+  const int64_t p = seqs.q_pos0[b] + (i - seqs.q_start[b]);
+  const uint16_t* lat = latent + seqs.k_start[b] * kDqk;
+  const int c = lane & 15, g = lane >> 4;
+  const int head0 = 16 * HG * pair;
+
+  const int nblk_total = (k + kBlk - 1) / kBlk;
+  const int per = (nblk_total + splits - 1) / splits;
+  const int blk_lo = min(nblk_total, split * per);
+  const int blk_hi = min(nblk_total, blk_lo + per);
+
+  // the row's index list, with invisible or out-of-range entries marked -1
+  const int32_t* irow = idx + i * (int64_t)k;
+  for (int j = tid; j < nblk_total * kBlk; j += blockDim.x) {
+    const int32_t s = j < k ? irow[j] : -1;
+    sm.idx[j] = (s >= 0 && s <= p) ? s : -1;
+  }
+
+  // q slice: B operand of QK; lane -> head (16hg + c), columns 288 vh + 32 ks + 8 g .. +8
+  i32x4 qf[HG][9];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    const uint16_t* qrow = q + (i * n_h + head0 + 16 * hg + c) * kDqk + 288 * vh + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) qf[hg][ks] = *reinterpret_cast<const i32x4*>(qrow + 32 * ks);
+  }
+  f32x4 o[HG][16];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+    for (int vt = 0; vt < 16; ++vt) o[hg][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[HG], l[HG];
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    m[hg] = -INFINITY;
+    l[hg] = 0.f;
+  }
+  __syncthreads();
+
+  // direct global->LDS gather of block blk into buffer bi (invalid slots load row 0
+  // of the sequence, which always exists; their scores are masked below)
+  auto gather = [&](int blk, int bi) {
+    for (int j = wave; j < kTileIns; j += nwaves) {
+      const int qg = 64 * j + lane;
+      const int r = qg / kGran, chunk = qg % kGran;
+      // pad granules (chunk 72, rows past the block) fetch an in-bounds granule of row 0
+      const bool real = r < kBlk && chunk < kDqk / 8;
+      const int s = real ? sm.idx[blk * kBlk + r] : -1;
+      const uint16_t* src = lat + (int64_t)(s >= 0 ? s : 0) * kDqk + (real ? 8 * chunk : 0);
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&sm.tile[bi][1024 * j], 16, 0,
+                                       0);
+    }
+  };
+
+  if (blk_lo < blk_hi) gather(blk_lo, 0);
+  for (int blk = blk_lo; blk < blk_hi; ++blk) {
+    const int bi = (blk - blk_lo) & 1;
+    __syncthreads();  // block blk landed for every wave; buffer bi^1 is free again
+    if (blk + 1 < blk_hi) gather(blk + 1, bi ^ 1);
+    const uint8_t* tile = sm.tile[bi];
+
+    // ---- partial S^T over this wave's 288 columns, for two 16-key tiles
+    f32x4 st[HG][2];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) st[hg][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int row = 16 * kt + c;
+        const i32x4 kf = *reinterpret_cast<const i32x4*>(tile + tile_off(row, 36 * vh + 4 * ks + g));
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg) st[hg][kt] = mfma_bf16_16x16x32(kf, qf[hg][ks], st[hg][kt]);
+      }
+    }
+    // ---- exchange partial scores with the partner wave
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) sm.xs[wave][2 * hg + kt][lane] = st[hg][kt];
+    __syncthreads();
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) st[hg][kt] += sm.xs[wave ^ 1][2 * hg + kt][lane];
+
+    // ---- online softmax (identical in both waves of the pair)
+    bool okr[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) okr[kt][r] = sm.idx[blk * kBlk + 16 * kt + 4 * g + r] >= 0;
+    i32x4 pf[HG];
+#pragma unroll
+    for (int hg = 0; hg < HG; ++hg) {
+      float x[2][4];
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[kt][r] = okr[kt][r] ? st[hg][kt][r] * scale_log2 : -INFINITY;
+          bmax = fmaxf(bmax, x[kt][r]);
+        }
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      if (__any(bmax > m[hg] + kLazy)) {
+        const float mnew = fmaxf(m[hg], bmax);
+        const float alpha = (m[hg] == -INFINITY) ? 0.f : exp2f(m[hg] - mnew);
+        m[hg] = mnew;
+        l[hg] *= alpha;
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
+#pragma unroll
+        for (int vt = 0; vt < 16; ++vt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[hg][vt][r] *= ar[r];
+      }
+      uint32_t pb[2][4];
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float pr = (m[hg] == -INFINITY) ? 0.f : exp2f(x[kt][r] - m[hg]);
+          pb[kt][r] = f32_to_bf16_bits(pr);
+          psum += __uint_as_float(pb[kt][r] << 16);
+        }
+      l[hg] += psum;
+      pf[hg] = i32x4{(int)(pb[0][0] | (pb[0][1] << 16)), (int)(pb[0][2] | (pb[0][3] << 16)),
+                     (int)(pb[1][0] | (pb[1][1] << 16)), (int)(pb[1][2] | (pb[1][3] << 16))};
+    }
+
+    // ---- O += P V over this wave's 256 value columns.  B operand via transpose
+    // reads: in each 16-lane group g, lane a + 4j reads 4 consecutive columns
+    // (16 vt + 4a ..) of key row 4g + j (slots 0-3) and 16 + 4g + j (slots 4-7).
+    const int ta = c & 3, tj = c >> 2;
+#pragma unroll
+    for (int vt = 0; vt < 16; ++vt) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int col = 256 * vh + 16 * vt + 4 * ta;
+      const int chunk = col >> 3, sub = (col & 7) * 2;
+      const int r0 = 4 * g + tj, r1 = 16 + 4 * g + tj;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + tile_off(r0, chunk) + sub));
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + tile_off(r1, chunk) + sub));
+      const i32x4 vf = i32x4{(int)(((uint32_t)(uint16_t)lo[0]) | ((uint32_t)(uint16_t)lo[1] << 16)),
+                             (int)(((uint32_t)(uint16_t)lo[2]) | ((uint32_t)(uint16_t)lo[3] << 16)),
+                             (int)(((uint32_t)(uint16_t)hi[0]) | ((uint32_t)(uint16_t)hi[1] << 16)),
+                             (int)(((uint32_t)(uint16_t)hi[2]) | ((uint32_t)(uint16_t)hi[3] << 16))};
+#pragma unroll
+      for (int hg = 0; hg < HG; ++hg) o[hg][vt] = mfma_bf16_16x16x32(pf[hg], vf, o[hg][vt]);
+    }
+  }
+
+  // ---- finish
+#pragma unroll
+  for (int hg = 0; hg < HG; ++hg) {
+    float lt = l[hg];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (splits == 1) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ir = __shfl(inv, 4 * g + r);
+        const int64_t orow = (i * n_h + head0 + 16 * hg + 4 * g + r) * kDv + 256 * vh;
+#pragma unroll
+        for (int vt = 0; vt < 16; ++vt) {
+          const float val = o[hg][vt][r] * ir;
+          if (out_f32)
+            out_f32[orow + 16 * vt + c] = val;
+          else
+            out_bf16[orow + 16 * vt + c] = (uint16_t)f32_to_bf16_bits(val);
+        }
+      }
+    } else {
+      const int64_t pbase = (i * splits + split) * (int64_t)n_h;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t orow = (pbase + head0 + 16 * hg + 4 * g + r) * kDv + 256 * vh;
+#pragma unroll
+        for (int vt = 0; vt < 16; ++vt) part_o[orow + 16 * vt + c] = o[hg][vt][r];
+      }
+      if (vh == 0 && g == 0) {
+        part_ml[(pbase + head0 + 16 * hg + c) * 2 + 0] = m[hg];
+        part_ml[(pbase + head0 + 16 * hg + c) * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
 // Merge split partials: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L.
 __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml, int n_h,
@@ -291,13 +534,20 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
     part_o = (float*)ws;
     part_ml = part_o + (size_t)n_q * splits * a.n_h * kDv;
   }
-  // 16 heads per wave: the Q slice (72 VGPRs) and the O accumulator (128) stay
-  // resident with two waves per SIMD and no spills.
-  const int waves = a.n_h / 16;
   dim3 grid((unsigned)(n_q * splits));
-  hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(64 * waves), 0, st, a.q, a.latent, a.idx, a.n_h, a.k,
-                     scale_log2, a.seqs, n_q, splits, splits == 1 ? out_f32 : nullptr,
-                     splits == 1 ? out_bf16 : nullptr, part_o, part_ml);
+  if (a.n_h % 32 == 0 && a.k <= kIdxMax) {
+    // wave pairs of 32 heads: 2 * n_h / 32 waves
+    hipLaunchKernelGGL(sparse_attn_pair_kernel<2>, grid, dim3(64 * (a.n_h / 16)), 0, st, a.q, a.latent, a.idx,
+                       a.n_h, a.k, scale_log2, a.seqs, n_q, splits, splits == 1 ? out_f32 : nullptr,
+                       splits == 1 ? out_bf16 : nullptr, part_o, part_ml);
+  } else {
+    // 16 heads per wave: the Q slice (72 VGPRs) and the O accumulator (128) stay
+    // resident with two waves per SIMD and no spills.
+    const int waves = a.n_h / 16;
+    hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(64 * waves), 0, st, a.q, a.latent, a.idx, a.n_h, a.k,
+                       scale_log2, a.seqs, n_q, splits, splits == 1 ? out_f32 : nullptr,
+                       splits == 1 ? out_bf16 : nullptr, part_o, part_ml);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3((unsigned)(n_q * a.n_h)), dim3(256), 0, st, part_o, part_ml,

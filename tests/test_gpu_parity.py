@@ -228,3 +228,20 @@ def test_all_f_runs_every_indexer_and_chunking_is_invisible():
     torch.cuda.synchronize()
     assert torch.allclose(res.outs[1][: 700 - 512], full.outs[1][last], rtol=0, atol=5e-3)
     assert torch.equal(res.index_cache[: 700 - 512], full.index_cache[last])
+
+
+def test_attention_large_budget_fallback():
+    """k above the paired kernel's LDS index capacity takes the 16-heads-per-wave kernel."""
+    announce("attention k=2100")
+    L, k = 2300, 2100
+    li = layer(L, 8, 64, 32, wid=1, layer_id=5)
+    g = np.random.default_rng(5)
+    idx = np.full((L, k), -1, np.int32)
+    for t in range(L):
+        m = min(k, t + 1)
+        idx[t, :m] = np.sort(g.choice(t + 1, size=m, replace=False))
+    idx_t = torch.from_numpy(idx).to(DEV)
+    seqs = dsa.Seqs.prefill(L)
+    out = dsa.sparse_attn(li.q, li.latent, idx_t, seqs)
+    torch.cuda.synchronize()
+    check_attention(OracleView(li), seqs, [0, 5, 2047, 2048, 2099, 2100, 2299], idx_t, out, 576 ** -0.5)
