@@ -232,21 +232,23 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
 // ----------------------------------------------------------------------------
 // Paired-wave variant (n_h a multiple of 32, k <= kIdxMax).
 //
-// A pair of waves owns 16*HG heads.  QK is split over the 576 latent columns
-// (wave vh takes columns [288 vh, 288 vh + 288)), so each wave keeps only half of
-// its heads' q in registers; the two partial score tiles are summed through LDS,
-// after which both waves hold identical scores and run the same softmax.  PV is
-// split over the value columns (wave vh accumulates columns [256 vh, 256 vh + 256)),
-// so each wave's O accumulator is 16*HG x 256.
+// A pair of waves owns 16*HG heads.  QK is split over the 576 latent columns in
+// alternating 32-column steps (wave vh takes steps 2 ks + vh), so each wave keeps
+// only half of its heads' q in registers; the two partial score tiles are summed
+// through LDS, after which both waves hold identical scores and run the same
+// softmax.  PV is split over alternating 16-column value tiles (wave vh takes
+// tiles 2 vt + vh), so each wave's O accumulator is 16*HG x 256.
 // Latent rows are gathered with direct global->LDS loads (no registers), one
 // block ahead of the block being computed, into a row-major tile padded to 73
 // granules per row (conflict-free b128 reads across 16 rows); V is read back
 // column-wise with the LDS transpose read, so no transposed copy is written.
 // ----------------------------------------------------------------------------
-constexpr int kGran = kDqk / 8 + 1;               // 16-byte granules per LDS row (72 + 1 pad)
-constexpr int kRowBytes = kGran * 16;             // 1168: rows land on distinct banks
-constexpr int kTileIns = (kBlk * kGran + 63) / 64;  // 64-lane x 16-byte loads per block (37)
-constexpr int kTileBytes = kTileIns * 1024;       // the last load spills into the tail pad
+// LDS tile of one block: 9 column groups of 128 bytes (8 granules of 16 B) x 32
+// rows; inside a row the 8 granules are XOR-swizzled by (row & 7), so 16 rows
+// read at one column land on distinct banks (pairs of rows 8 apart share).
+constexpr int kCg = kDqk / 64;                    // 9 column groups
+constexpr int kTileBytes = kCg * kBlk * 128;      // 36864
+constexpr int kTileIns = kTileBytes / 1024;       // 36 64-lane x 16-byte copies per block
 constexpr int kNBuf = 2;
 constexpr int kIdxMax = 2048;
 constexpr int kMaxWaves = 8;
@@ -260,7 +262,37 @@ struct PairSmem {
   int idx[kIdxMax];             // the row's selected positions (-1 = skip)
 };
 
-__device__ __forceinline__ uint32_t tile_off(int row, int chunk) { return (uint32_t)(row * kRowBytes + 16 * chunk); }
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt), not for outstanding global->LDS copies (vmcnt).  The "memory"
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Four LDS transpose reads (4 x b16 each) and the wait for them, in one asm
+// block: the compiler cannot tell these reads from the buffer being filled by
+// the asynchronous gather and would otherwise wait for that gather first.
+__device__ __forceinline__ void tr16_x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint64_t& d0,
+                                        uint64_t& d1, uint64_t& d2, uint64_t& d3) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %5\n\t"
+      "ds_read_b64_tr_b16 %2, %6\n\t"
+      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
+}
+
+__device__ __forceinline__ i32x4 pack_tr(uint64_t lo, uint64_t hi) {
+  return i32x4{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
+}
+
+__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
+  return (uint32_t)((chunk >> 3) * (kBlk * 128) + row * 128 + 16 * ((chunk & 7) ^ (row & 7)));
+}
 
 template <int HG>
 __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* __restrict__ q,
@@ -295,13 +327,14 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
     sm.idx[j] = (s >= 0 && s <= p) ? s : -1;
   }
 
-  // q slice: B operand of QK; lane -> head (16hg + c), columns 288 vh + 32 ks + 8 g .. +8
+  // q slice: B operand of QK; lane -> head (16hg + c); this wave takes the 32-column
+  // steps 2 ks + vh (columns 64 ks + 32 vh + 8 g .. +8)
   i32x4 qf[HG][9];
 #pragma unroll
   for (int hg = 0; hg < HG; ++hg) {
-    const uint16_t* qrow = q + (i * n_h + head0 + 16 * hg + c) * kDqk + 288 * vh + 8 * g;
+    const uint16_t* qrow = q + (i * n_h + head0 + 16 * hg + c) * kDqk + 32 * vh + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < 9; ++ks) qf[hg][ks] = *reinterpret_cast<const i32x4*>(qrow + 32 * ks);
+    for (int ks = 0; ks < 9; ++ks) qf[hg][ks] = *reinterpret_cast<const i32x4*>(qrow + 64 * ks);
   }
   f32x4 o[HG][16];
 #pragma unroll
@@ -318,14 +351,15 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
 
   // direct global->LDS gather of block blk into buffer bi (invalid slots load row 0
   // of the sequence, which always exists; their scores are masked below)
+  // copy j fills column group j/4, rows 8(j%4) .. +8; lane l lands in row
+  // 8(j%4) + l/8 at swizzled position l%8, i.e. it fetches granule (l%8) ^ (row & 7)
+  const int lrow = lane >> 3, lpos = lane & 7;
   auto gather = [&](int blk, int bi) {
     for (int j = wave; j < kTileIns; j += nwaves) {
-      const int qg = 64 * j + lane;
-      const int r = qg / kGran, chunk = qg % kGran;
-      // pad granules (chunk 72, rows past the block) fetch an in-bounds granule of row 0
-      const bool real = r < kBlk && chunk < kDqk / 8;
-      const int s = real ? sm.idx[blk * kBlk + r] : -1;
-      const uint16_t* src = lat + (int64_t)(s >= 0 ? s : 0) * kDqk + (real ? 8 * chunk : 0);
+      const int r = 8 * (j & 3) + lrow;
+      const int chunk = 8 * (j >> 2) + (lpos ^ (r & 7));
+      const int s = sm.idx[blk * kBlk + r];
+      const uint16_t* src = lat + (int64_t)(s >= 0 ? s : 0) * kDqk + 8 * chunk;
       __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&sm.tile[bi][1024 * j], 16, 0,
                                        0);
     }
@@ -344,13 +378,13 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
     for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) st[hg][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // K fragment of step ks: column group ks, granule 4 vh + g of row 16 kt + c
+    const uint8_t* kbase = tile + c * 128 + 16 * ((4 * vh + g) ^ (c & 7));
 #pragma unroll
     for (int ks = 0; ks < 9; ++ks) {
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const int row = 16 * kt + c;
-        const i32x4 kf = *reinterpret_cast<const i32x4*>(tile + tile_off(row, 36 * vh + 4 * ks + g));
+        const i32x4 kf = *reinterpret_cast<const i32x4*>(kbase + ks * (kBlk * 128) + kt * 2048);
 #pragma unroll
         for (int hg = 0; hg < HG; ++hg) st[hg][kt] = mfma_bf16_16x16x32(kf, qf[hg][ks], st[hg][kt]);
       }
@@ -360,7 +394,7 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
     for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) sm.xs[wave][2 * hg + kt][lane] = st[hg][kt];
-    __syncthreads();
+    lds_barrier();  // waits for LDS traffic only, not for the next block's gather
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
@@ -399,39 +433,43 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
 #pragma unroll
           for (int r = 0; r < 4; ++r) o[hg][vt][r] *= ar[r];
       }
-      uint32_t pb[2][4];
+      // p = 2^(x - m) (x = -inf gives 0), rounded once to bf16 pairs; the
+      // normaliser sums the rounded values
+      const float mu = (m[hg] == -INFINITY) ? 0.f : m[hg];
       float psum = 0.f;
+      uint32_t pk[4];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pr = (m[hg] == -INFINITY) ? 0.f : exp2f(x[kt][r] - m[hg]);
-          pb[kt][r] = f32_to_bf16_bits(pr);
-          psum += __uint_as_float(pb[kt][r] << 16);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int kt = e >> 1, r = 2 * (e & 1);
+        const bf16x2 v = {(__bf16)__builtin_amdgcn_exp2f(x[kt][r] - mu),
+                          (__bf16)__builtin_amdgcn_exp2f(x[kt][r + 1] - mu)};
+        pk[e] = __builtin_bit_cast(uint32_t, v);
+        psum += __uint_as_float(pk[e] << 16) + __uint_as_float(pk[e] & 0xFFFF0000u);
+      }
       l[hg] += psum;
-      pf[hg] = i32x4{(int)(pb[0][0] | (pb[0][1] << 16)), (int)(pb[0][2] | (pb[0][3] << 16)),
-                     (int)(pb[1][0] | (pb[1][1] << 16)), (int)(pb[1][2] | (pb[1][3] << 16))};
+      pf[hg] = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
     }
 
-    // ---- O += P V over this wave's 256 value columns.  B operand via transpose
-    // reads: in each 16-lane group g, lane a + 4j reads 4 consecutive columns
-    // (16 vt + 4a ..) of key row 4g + j (slots 0-3) and 16 + 4g + j (slots 4-7).
+    // ---- O += P V over this wave's value tiles 2 vt + vh (columns 32 vt + 16 vh + ..).
+    // B operand via transpose reads: in 16-lane group g, lane a + 4j reads 4 columns
+    // (.. + 4a) of key row 4g + j (K slots 0-3) and of row 16 + 4g + j (slots 4-7).
     const int ta = c & 3, tj = c >> 2;
+    const int r0 = 4 * g + tj;
+    const uint8_t* vb0 = tile + r0 * 128 + 16 * ((2 * vh + (ta >> 1)) ^ (r0 & 7)) + 8 * (ta & 1);
+    const uint8_t* vb1 = tile + r0 * 128 + 16 * ((4 + 2 * vh + (ta >> 1)) ^ (r0 & 7)) + 8 * (ta & 1);
+    const uint32_t va0 = lds_addr(vb0), va1 = lds_addr(vb1);
 #pragma unroll
-    for (int vt = 0; vt < 16; ++vt) {
-      __builtin_amdgcn_sched_barrier(0);
-      const int col = 256 * vh + 16 * vt + 4 * ta;
-      const int chunk = col >> 3, sub = (col & 7) * 2;
-      const int r0 = 4 * g + tj, r1 = 16 + 4 * g + tj;
-      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + tile_off(r0, chunk) + sub));
-      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(tile + tile_off(r1, chunk) + sub));
-      const i32x4 vf = i32x4{(int)(((uint32_t)(uint16_t)lo[0]) | ((uint32_t)(uint16_t)lo[1] << 16)),
-                             (int)(((uint32_t)(uint16_t)lo[2]) | ((uint32_t)(uint16_t)lo[3] << 16)),
-                             (int)(((uint32_t)(uint16_t)hi[0]) | ((uint32_t)(uint16_t)hi[1] << 16)),
-                             (int)(((uint32_t)(uint16_t)hi[2]) | ((uint32_t)(uint16_t)hi[3] << 16))};
+    for (int vt = 0; vt < 16; vt += 2) {
+      // tiles vt (even: base 0) and vt + 1 (odd: base 1) share column group vt / 2
+      const uint32_t cgo = (vt >> 1) * (kBlk * 128);
+      uint64_t e0, e1, d0, d1;
+      tr16_x4(va0 + cgo, va0 + cgo + 2048, va1 + cgo, va1 + cgo + 2048, e0, e1, d0, d1);
+      const i32x4 vfe = pack_tr(e0, e1), vfo = pack_tr(d0, d1);
 #pragma unroll
-      for (int hg = 0; hg < HG; ++hg) o[hg][vt] = mfma_bf16_16x16x32(pf[hg], vf, o[hg][vt]);
+      for (int hg = 0; hg < HG; ++hg) {
+        o[hg][vt] = mfma_bf16_16x16x32(pf[hg], vfe, o[hg][vt]);
+        o[hg][vt + 1] = mfma_bf16_16x16x32(pf[hg], vfo, o[hg][vt + 1]);
+      }
     }
   }
 
@@ -446,23 +484,23 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float ir = __shfl(inv, 4 * g + r);
-        const int64_t orow = (i * n_h + head0 + 16 * hg + 4 * g + r) * kDv + 256 * vh;
+        const int64_t orow = (i * n_h + head0 + 16 * hg + 4 * g + r) * kDv + 16 * vh + c;
 #pragma unroll
         for (int vt = 0; vt < 16; ++vt) {
           const float val = o[hg][vt][r] * ir;
           if (out_f32)
-            out_f32[orow + 16 * vt + c] = val;
+            out_f32[orow + 32 * vt] = val;
           else
-            out_bf16[orow + 16 * vt + c] = (uint16_t)f32_to_bf16_bits(val);
+            out_bf16[orow + 32 * vt] = (uint16_t)f32_to_bf16_bits(val);
         }
       }
     } else {
       const int64_t pbase = (i * splits + split) * (int64_t)n_h;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t orow = (pbase + head0 + 16 * hg + 4 * g + r) * kDv + 256 * vh;
+        const int64_t orow = (pbase + head0 + 16 * hg + 4 * g + r) * kDv + 16 * vh + c;
 #pragma unroll
-        for (int vt = 0; vt < 16; ++vt) part_o[orow + 16 * vt + c] = o[hg][vt][r];
+        for (int vt = 0; vt < 16; ++vt) part_o[orow + 32 * vt] = o[hg][vt][r];
       }
       if (vh == 0 && g == 0) {
         part_ml[(pbase + head0 + 16 * hg + c) * 2 + 0] = m[hg];
