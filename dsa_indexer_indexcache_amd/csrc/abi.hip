@@ -55,8 +55,19 @@ int check_seqs(const dsa_seqs* s, int64_t* n_q, int64_t* n_k) {
 
 int heads_supported(int H) { return H >= 1 && H <= 64; }
 
-size_t indexer_ws(int64_t n_q, const dsa_seqs& s) {
-  if (n_q == 0) return 0;
+dsa::IndexerArgs shape_args(int qk_dtype, int H, int d, int k, const dsa_seqs& s) {
+  dsa::IndexerArgs a{};
+  a.qk_dtype = qk_dtype;
+  a.H = H;
+  a.d = d;
+  a.k = k;
+  a.seqs = s;
+  return a;
+}
+
+// The fused kernel needs no workspace; the slab path keeps one fp32 score per visible pair of a row.
+size_t indexer_ws(int64_t n_q, const dsa_seqs& s, int qk_dtype, int H, int d, int k) {
+  if (n_q == 0 || dsa::indexer_fused_ok(shape_args(qk_dtype, H, d, k, s))) return 0;
   return (size_t)n_q * (size_t)dsa::slab_ld(s) * sizeof(float) + 256;
 }
 
@@ -116,6 +127,11 @@ dsa::IndexerArgs indexer_args(const void* q_idx, const float* q_scale, const voi
 }
 
 int run_indexer(const dsa::IndexerArgs& a, void* ws, hipStream_t st) {
+  if (dsa::indexer_fused_ok(a)) {
+    hipError_t e = dsa::launch_indexer_fused(a, st);
+    if (e != hipSuccess) return hip_fail(e, "fused indexer launch");
+    return DSA_OK;
+  }
   float* slab = (float*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
   hipError_t e = dsa::launch_indexer_slab(a, slab, st);
   if (e != hipSuccess) return hip_fail(e, "indexer score launch");
@@ -210,13 +226,9 @@ int indexcache_plan(const char* roles, int32_t* src_layer, int32_t* n_indexer_ca
 }
 
 size_t dsa_indexer_topk_ws(int qk_dtype, int H, int d, int k, const dsa_seqs* seqs) {
-  (void)qk_dtype;
-  (void)H;
-  (void)d;
-  (void)k;
   int64_t n_q, n_k;
   if (check_seqs(seqs, &n_q, &n_k) != DSA_OK) return 0;
-  return indexer_ws(n_q, *seqs);
+  return indexer_ws(n_q, *seqs, qk_dtype, H, d, k);
 }
 
 int dsa_indexer_topk(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
@@ -230,7 +242,7 @@ int dsa_indexer_topk(const void* q_idx, const float* q_scale, const void* k_idx,
   if (n_q == 0) return DSA_OK;
   if (!idx_out) return fail(DSA_ERR_INVALID_ARG, "idx_out is required");
   if (((uintptr_t)idx_out & 3u) || ((uintptr_t)score_out & 3u)) return fail(DSA_ERR_ALIGNMENT, "outputs misaligned");
-  const size_t need = indexer_ws(n_q, *seqs);
+  const size_t need = indexer_ws(n_q, *seqs, qk_dtype, H, d, k);
   if (ws_bytes < need || (need && !ws)) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   return run_indexer(indexer_args(q_idx, q_scale, k_idx, k_scale, w, qk_dtype, H, d, k, *seqs, idx_out, score_out),
                      ws, (hipStream_t)stream);
@@ -276,7 +288,7 @@ size_t indexcache_forward_ws(const char* roles, const dsa_shape* shape, const ds
   for (int64_t r0 = 0; r0 < n_q; r0 += shape->q_chunk) {
     const int64_t r1 = r0 + shape->q_chunk < n_q ? r0 + shape->q_chunk : n_q;
     const dsa_seqs cs = slice_seqs(*seqs, r0, r1);
-    size_t a = indexer_ws(r1 - r0, cs);
+    size_t a = indexer_ws(r1 - r0, cs, shape->qk_dtype, shape->H, shape->d, shape->k);
     size_t b = dsa::attn_ws_bytes(attn_args(nullptr, nullptr, nullptr, shape->n_h, shape->d_qk, shape->d_v,
                                             shape->k, shape->scale, cs, nullptr, shape->out_dtype));
     mx = mx > a ? mx : a;

@@ -1,0 +1,456 @@
+// Fused lightning indexer + streaming top-k for prefill (one sequence, many queries).
+//
+// Score ([IDX] §4 lightning-indexer equation) I[t,s] = sum_j w[t,j] ReLU(q_idx[t,j,:] . k_idx[s,:])
+// for the visible keys s <= t, and S_t = the k best (score desc, position asc)
+// ([IDX] §2 TopK; §6.5 deterministic), without ever writing the score matrix.
+//
+// Workgroup: 8 waves, one query row per wave (8 consecutive rows), heaviest rows
+// first.  Keys stream through LDS in tiles of 64 (direct global->LDS copies, one
+// tile ahead); every wave scores its query against the tile:
+//   MFMA   rows = 16 indexer heads, columns = 16 keys, K = head dim (fp8: one
+//          v_mfma_f32_16x16x128_f8f6f4 per 16x16 tile; bf16: d/32 x 16x16x32);
+//   head sum: lane (g, c) holds heads 4g+r of key c; it folds ReLU and w in
+//          registers, and two permlane32 swaps plus one permlane16 swap finish the
+//          sum so that lane l ends with the score of key 64T + l;
+//   filter: a key is a candidate only if its order key exceeds the current
+//          threshold; candidates are appended to a per-wave pending list in LDS.
+// The exact top-k state (2048 (key, position) pairs) lives in registers, 32 per
+// lane.  When the pending list fills, a wave-level radix select on the 64-bit key
+// (order(score) << 32 | ~position) over state + pending finds the k-th best, keeps
+// exactly the k best and raises the threshold to that element's score key.
+// Keys arrive in increasing position, so a later key that ties the threshold
+// score always loses the tie: the strict filter is exact.
+#include "dsa_device.h"
+#include "launch.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kFT = 64;         // keys per tile
+constexpr int kFW = 8;          // waves (= query rows) per workgroup
+constexpr int kSlots = 32;      // state slots per lane: 2048 per wave
+constexpr int kPendCap = 1024;  // pending candidates per wave
+
+template <bool FP8, int D>
+struct FCfg {
+  static constexpr int row_bytes = FP8 ? D : 2 * D;           // one key row in LDS
+  static constexpr int tile_bytes = kFT * row_bytes;
+  static constexpr int dma_per_tile = tile_bytes / 1024;     // 64 lanes x 16 B copies
+  static constexpr int gran = row_bytes / 16;
+};
+
+template <bool FP8, int D>
+struct FusedSmem {
+  uint8_t tile[2][FCfg<FP8, D>::tile_bytes];
+  float kscale[2][kFT];
+  uint32_t pkey[kFW][kPendCap];
+  uint32_t ppos[kFW][kPendCap];
+  uint32_t hist[kFW][256];
+};
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 64-lane global->LDS copy of 16 (or 4) bytes per lane to lds_base + lane * size,
+// issued from asm so that the compiler does not attach waits for it to unrelated
+// LDS reads; completion is awaited by the s_waitcnt vmcnt(0) before the next
+// workgroup barrier.  M0 is saved and restored.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+__device__ __forceinline__ uint64_t key64(uint32_t key, uint32_t pos) {
+  return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - pos);
+}
+
+__device__ __forceinline__ float key_to_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Moves pending entries [0, n) into the free (key == 0) state slots, lane by lane.
+__device__ __forceinline__ void fill_free(uint32_t (&skey)[kSlots], uint32_t (&spos)[kSlots], const uint32_t* pkey,
+                                          const uint32_t* ppos, int n, int lane) {
+  int freec = 0;
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) freec += skey[j] == 0u;
+  // exclusive prefix of free counts over lanes
+  int incl = freec;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  int cur = incl - freec;
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    if (skey[j] == 0u && cur < n) {
+      skey[j] = pkey[cur];
+      spos[j] = ppos[cur];
+      ++cur;
+    }
+  }
+}
+
+// Keeps exactly the k best of state + pending and returns the new threshold key.
+// Wave-level; uses this wave's histogram and pending areas of LDS only.
+__device__ uint32_t compact(uint32_t (&skey)[kSlots], uint32_t (&spos)[kSlots], uint32_t* pkey, uint32_t* ppos,
+                           uint32_t* hist, int n_pend, int& n_state, uint32_t theta, int k, int lane) {
+  if (n_state + n_pend <= k) {
+    fill_free(skey, spos, pkey, ppos, n_pend, lane);
+    n_state += n_pend;
+    return theta;
+  }
+  // radix select of the k-th largest 64-bit key, 8 bits at a time, most significant first
+  uint64_t prefix = 0, pmask = 0;
+  uint32_t remaining = (uint32_t)k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0u;
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      const uint64_t kk = key64(skey[j], spos[j]);
+      if (skey[j] != 0u && (kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+    }
+    for (int p = lane; p < n_pend; p += 64) {
+      const uint64_t kk = key64(pkey[p], ppos[p]);
+      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+    }
+    uint32_t h[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) h[b] = hist[4 * lane + b];
+    const uint32_t local = h[0] + h[1] + h[2] + h[3];
+    uint32_t incl = local;  // suffix sum over lanes: bins >= 4 lane
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_down(incl, d);
+      if (lane + d < 64) incl += o;
+    }
+    uint32_t above = incl - local;  // bins > 4 lane + 3
+    int found = -1;
+    uint32_t f_above = 0, f_cnt = 0;
+#pragma unroll
+    for (int b = 3; b >= 0; --b) {
+      if (found < 0 && above < remaining && remaining <= above + h[b]) {
+        found = 4 * lane + b;
+        f_above = above;
+        f_cnt = h[b];
+      }
+      above += h[b];
+    }
+    const uint64_t ball = __ballot(found >= 0);
+    const int src = __ffsll((long long)ball) - 1;
+    const uint32_t digit = (uint32_t)__shfl(found, src);
+    const uint32_t ab = __shfl(f_above, src);
+    const uint32_t cnt = __shfl(f_cnt, src);
+    prefix |= (uint64_t)digit << shift;
+    pmask |= (uint64_t)0xFFu << shift;
+    remaining -= ab;
+    if (cnt == remaining) break;  // every key in this bin is selected
+  }
+  const uint64_t th = prefix;  // selected  <=>  key64 >= th  (exactly k keys)
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j)
+    if (skey[j] != 0u && key64(skey[j], spos[j]) < th) skey[j] = 0u;
+  // pack the selected pending entries to the front, in place (writes trail reads)
+  int kept = 0;
+  for (int base = 0; base < n_pend; base += 64) {
+    const int p = base + lane;
+    uint32_t kk = 0, pp = 0;
+    bool sel = false;
+    if (p < n_pend) {
+      kk = pkey[p];
+      pp = ppos[p];
+      sel = key64(kk, pp) >= th;
+    }
+    const uint64_t m = __ballot(sel);
+    if (sel) {
+      const int dst = kept + (int)__popcll(m & ((1ull << lane) - 1ull));
+      pkey[dst] = kk;
+      ppos[dst] = pp;
+    }
+    kept += (int)__popcll(m);
+  }
+  fill_free(skey, spos, pkey, ppos, kept, lane);
+  n_state = k;
+  return (uint32_t)(th >> 32);
+}
+
+template <int HB, bool FP8, int D>
+__global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restrict__ q_idx,
+                                                             const float* __restrict__ q_scale,
+                                                             const void* __restrict__ k_idx,
+                                                             const float* __restrict__ k_scale,
+                                                             const uint16_t* __restrict__ w, int H, int k,
+                                                             int64_t n_q, int64_t q_pos0, int64_t k_row0,
+                                                             int64_t n_keys, int32_t* __restrict__ idx_out,
+                                                             float* __restrict__ score_out) {
+  using C = FCfg<FP8, D>;
+  __shared__ FusedSmem<FP8, D> sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int64_t n_groups = (n_q + kFW - 1) / kFW;
+  const int64_t grp = n_groups - 1 - (int64_t)blockIdx.x;  // heaviest rows first
+  const int64_t i0 = grp * kFW;
+  const int64_t i = i0 + wave;
+  const bool row_ok = i < n_q;
+  const int64_t t = row_ok ? q_pos0 + i : -1;                         // this wave's position
+  const int64_t t_max = q_pos0 + (i0 + kFW - 1 < n_q ? i0 + kFW - 1 : n_q - 1);
+  const int n_tiles = (int)((t_max + kFT) / kFT);
+  const uint8_t* kbytes = (const uint8_t*)k_idx + k_row0 * C::row_bytes;
+  const float* kscale_g = FP8 ? k_scale + k_row0 : nullptr;
+
+  // ---- this row's q (A operand) and head weights w' = w * q_scale (heads 16hb + 4g + r)
+  constexpr int KS = FP8 ? 1 : D / 32;
+  i32x4 qa[HB][FP8 ? 2 : KS];
+  float wl[HB][4];
+  const int64_t qi = row_ok ? i : n_q - 1;
+  // padded heads (H < 16 HB) read a real head's q and get weight 0
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int head = min(16 * hb + c, H - 1);
+    if constexpr (FP8) {
+      const i32x4* src = reinterpret_cast<const i32x4*>((const uint8_t*)q_idx + (qi * H + head) * D + 32 * g);
+      qa[hb][0] = src[0];
+      qa[hb][1] = src[1];
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qa[hb][ks] = *reinterpret_cast<const i32x4*>((const uint16_t*)q_idx + (qi * H + head) * D + 32 * ks + 8 * g);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hh = 16 * hb + 4 * g + r;
+      const int hc = min(hh, H - 1);
+      float wv = bf16_to_f32(w[qi * H + hc]);
+      if constexpr (FP8) wv *= q_scale[qi * H + hc];
+      wl[hb][r] = hh < H ? wv : 0.f;
+    }
+  }
+
+  // ---- key tiles: copy j of a tile covers LDS bytes [1024 j, 1024 j + 1024); lane l
+  // fills granule slot (l % gran) of row (1024 j / row_bytes + l / gran), holding the
+  // row's granule slot ^ (row & 7) (XOR swizzle: conflict-free B-operand reads)
+  auto issue_tile = [&](int T, int bi) {
+    for (int j = wave; j < C::dma_per_tile; j += kFW) {
+      const int r = j * (1024 / C::row_bytes) + lane / C::gran;
+      const int slot = lane % C::gran;
+      int64_t s = (int64_t)T * kFT + r;
+      if (s > n_keys - 1) s = n_keys - 1;  // tail rows past the keys: in-bounds, masked later
+      const uint8_t* src = kbytes + s * C::row_bytes + 16 * (slot ^ (r & 7));
+      dma16(src, lds_u32(&sm.tile[bi][1024 * j]));
+    }
+    if (FP8 && wave == kFW - 1) {
+      int64_t s = (int64_t)T * kFT + lane;
+      if (s > n_keys - 1) s = n_keys - 1;
+      dma4(kscale_g + s, lds_u32(&sm.kscale[bi][0]));
+    }
+  };
+
+  uint32_t skey[kSlots], spos[kSlots];
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    skey[j] = 0u;
+    spos[j] = 0u;
+  }
+  uint32_t* pkey = sm.pkey[wave];
+  uint32_t* ppos = sm.ppos[wave];
+  uint32_t* hist = sm.hist[wave];
+  int n_pend = 0, n_state = 0;
+  uint32_t theta = 0u;  // order keys of real scores are > 0: everything passes at first
+
+  issue_tile(0, 0);
+  for (int T = 0; T < n_tiles; ++T) {
+    const int bi = T & 1;
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile T landed
+    __syncthreads();                     // ... and every wave's; buffer bi^1 is free
+    if (T + 1 < n_tiles) issue_tile(T + 1, bi ^ 1);
+    const uint8_t* tile = sm.tile[bi];
+
+    float part[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int row = 16 * u + c;
+      const uint8_t* rb = tile + row * C::row_bytes;
+      f32x4 acc[HB];
+      if constexpr (FP8) {
+        const i32x4 b0 = *reinterpret_cast<const i32x4*>(rb + 16 * ((2 * g) ^ (row & 7)));
+        const i32x4 b1 = *reinterpret_cast<const i32x4*>(rb + 16 * ((2 * g + 1) ^ (row & 7)));
+        const i32x8 bf = i32x8{b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          const i32x8 af = i32x8{qa[hb][0][0], qa[hb][0][1], qa[hb][0][2], qa[hb][0][3],
+                                 qa[hb][1][0], qa[hb][1][1], qa[hb][1][2], qa[hb][1][3]};
+          acc[hb] = mfma_fp8_16x16x128(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+        }
+      } else {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const i32x4 bf = *reinterpret_cast<const i32x4*>(rb + 16 * ((4 * ks + g) ^ (row & 7)));
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16_16x16x32(qa[hb][ks], bf, acc[hb]);
+        }
+      }
+      float pv = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv += wl[hb][r] * fmaxf(acc[hb][r], 0.f);
+      part[u] = pv;
+    }
+    // ---- finish the head sum: lane (g, c) -> key 16 g + c of the tile (= lane)
+    const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+    const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+    const float s02 = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);
+    const float s13 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
+    const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+    float score = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    if constexpr (FP8) score *= sm.kscale[bi][lane];
+
+    // ---- filter into the pending list
+    const int64_t s = (int64_t)T * kFT + lane;
+    const uint32_t key = order_key(score);
+    const bool pass = s <= t && key > theta;
+    const uint64_t m = __ballot(pass);
+    if (pass) {
+      const int dst = n_pend + (int)__popcll(m & ((1ull << lane) - 1ull));
+      pkey[dst] = key;
+      ppos[dst] = (uint32_t)s;
+    }
+    n_pend += (int)__popcll(m);
+    if (n_pend > kPendCap - kFT) {
+      theta = compact(skey, spos, pkey, ppos, hist, n_pend, n_state, theta, k, lane);
+      n_pend = 0;
+    }
+  }
+  if (n_pend > 0) theta = compact(skey, spos, pkey, ppos, hist, n_pend, n_state, theta, k, lane);
+  if (!row_ok) return;
+
+  // ---- write the row (valid entries first, unordered; a row sort follows)
+  int v = 0;
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) v += skey[j] != 0u;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  int pos = incl - v;
+  int32_t* orow = idx_out + i * (int64_t)k;
+  float* srow = score_out ? score_out + i * (int64_t)k : nullptr;
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    if (skey[j] != 0u) {
+      orow[pos] = (int32_t)spos[j];
+      if (srow) srow[pos] = key_to_score(skey[j]);
+      ++pos;
+    }
+  }
+  for (int j = n_state + lane; j < k; j += 64) {
+    orow[j] = -1;
+    if (srow) srow[j] = 0.f;
+  }
+}
+
+// Sorts the valid prefix of each index row (positions ascending, scores follow).
+// One workgroup per row; bitonic sort of up to 2048 entries in LDS.
+__global__ __launch_bounds__(256) void idx_row_sort_kernel(int32_t* __restrict__ idx, float* __restrict__ score,
+                                                           int k, int64_t n_q) {
+  __shared__ int32_t sp[2048];
+  __shared__ float ss[2048];
+  const int64_t i = blockIdx.x;
+  if (i >= n_q) return;
+  int32_t* row = idx + i * (int64_t)k;
+  float* srow = score ? score + i * (int64_t)k : nullptr;
+  int n = 1;
+  while (n < k) n <<= 1;
+  for (int j = threadIdx.x; j < n; j += blockDim.x) {
+    const int32_t p = j < k ? row[j] : -1;
+    sp[j] = p < 0 ? INT32_MAX : p;
+    ss[j] = (j < k && srow) ? srow[j] : 0.f;
+  }
+  __syncthreads();
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int j = threadIdx.x; j < n / 2; j += blockDim.x) {
+        const int lo = 2 * j - (j & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const int32_t a = sp[lo], b = sp[hi];
+        if ((a > b) == up) {
+          sp[lo] = b;
+          sp[hi] = a;
+          const float fa = ss[lo];
+          ss[lo] = ss[hi];
+          ss[hi] = fa;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int j = threadIdx.x; j < k; j += blockDim.x) {
+    const int32_t p = sp[j];
+    row[j] = p == INT32_MAX ? -1 : p;
+    if (srow) srow[j] = p == INT32_MAX ? 0.f : ss[j];
+  }
+}
+
+}  // namespace
+
+bool indexer_fused_ok(const IndexerArgs& a) {
+  if (a.seqs.B != 1 || a.k > kSlots * 64) return false;
+  const int64_t n_q = a.seqs.q_start[1] - a.seqs.q_start[0];
+  if (n_q < 256) return false;
+  if (a.qk_dtype == DSA_FP8_E4M3) return a.d == 128;
+  return a.d == 64 || a.d == 128;
+}
+
+hipError_t launch_indexer_fused(const IndexerArgs& a, hipStream_t st) {
+  const int64_t n_q = a.seqs.q_start[1] - a.seqs.q_start[0];
+  const int64_t n_keys = a.seqs.k_start[1] - a.seqs.k_start[0];
+  const int HB = a.H <= 16 ? 1 : a.H <= 32 ? 2 : 4;
+  dim3 grid((unsigned)((n_q + kFW - 1) / kFW));
+  const bool fp8 = a.qk_dtype == DSA_FP8_E4M3;
+#define DSA_FUSED(HBv, F8, Dv)                                                                                 \
+  if (HB == HBv && fp8 == F8 && a.d == Dv) {                                                                  \
+    hipLaunchKernelGGL((idx_topk_fused_kernel<HBv, F8, Dv>), grid, dim3(64 * kFW), 0, st, a.q_idx, a.q_scale,   \
+                       a.k_idx, a.k_scale, a.w, a.H, a.k, n_q, a.seqs.q_pos0[0], a.seqs.k_start[0], n_keys,  \
+                       a.idx_out, a.score_out);                                                              \
+    found = true;                                                                                            \
+  }
+  bool found = false;
+  DSA_FUSED(1, true, 128) DSA_FUSED(2, true, 128) DSA_FUSED(4, true, 128)
+  DSA_FUSED(1, false, 128) DSA_FUSED(2, false, 128) DSA_FUSED(4, false, 128)
+  DSA_FUSED(1, false, 64) DSA_FUSED(2, false, 64) DSA_FUSED(4, false, 64)
+#undef DSA_FUSED
+  if (!found) return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(idx_row_sort_kernel, dim3((unsigned)n_q), dim3(256), 0, st, a.idx_out, a.score_out, a.k, n_q);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

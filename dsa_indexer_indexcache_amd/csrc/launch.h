@@ -36,6 +36,10 @@ int64_t slab_ld(const dsa_seqs& s);
 hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st);
 hipError_t launch_topk_select(const IndexerArgs& a, const float* slab, hipStream_t st);
 
+// indexer_fused.hip: one-sequence prefill, scores never leave the chip; no workspace.
+bool indexer_fused_ok(const IndexerArgs& a);
+hipError_t launch_indexer_fused(const IndexerArgs& a, hipStream_t st);
+
 // sparse_attn.hip
 int attn_splits(const AttnArgs& a);
 size_t attn_ws_bytes(const AttnArgs& a);
