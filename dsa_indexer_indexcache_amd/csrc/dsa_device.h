@@ -30,6 +30,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// ReLU of a finite float as a signed-integer max of its bit pattern: negative
+// values (sign bit set) and -0.0 become +0.0.  One v_max_i32, where fmaxf would
+// first canonicalise its input under IEEE mode.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Total order on fp32 scores as unsigned keys; -0.0 is first mapped to +0.0 so
 // the two zeros tie (the selection then falls back to position order).
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -30,7 +30,7 @@ namespace {
 constexpr int kFT = 64;         // keys per tile
 constexpr int kFW = 8;          // waves (= query rows) per workgroup
 constexpr int kSlots = 32;      // state slots per lane: 2048 per wave
-constexpr int kPendCap = 1024;  // pending candidates per wave
+constexpr int kPendCap = 1536;  // pending candidates per wave
 
 template <bool FP8, int D>
 struct FCfg {
@@ -40,13 +40,20 @@ struct FCfg {
   static constexpr int gran = row_bytes / 16;
 };
 
+// key tiles in LDS (the one being scored + ring-1 in flight): 4 small fp8 tiles or 2 bf16 tiles
+template <bool FP8, int D>
+constexpr int ring_of() {
+  return FCfg<FP8, D>::tile_bytes <= 8192 ? 4 : 2;
+}
+
 template <bool FP8, int D>
 struct FusedSmem {
-  uint8_t tile[2][FCfg<FP8, D>::tile_bytes];
-  float kscale[2][kFT];
+  uint8_t tile[ring_of<FP8, D>()][FCfg<FP8, D>::tile_bytes];
+  float kscale[ring_of<FP8, D>()][kFT];
   uint32_t pkey[kFW][kPendCap];
   uint32_t ppos[kFW][kPendCap];
   uint32_t hist[kFW][256];
+  int need[2][kFW];  // per-wave "pending list nearly full" votes, by tile parity
 };
 
 __device__ __forceinline__ uint32_t lds_u32(const void* p) {
@@ -55,13 +62,16 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 
 // 64-lane global->LDS copy of 16 (or 4) bytes per lane to lds_base + lane * size,
 // issued from asm so that the compiler does not attach waits for it to unrelated
-// LDS reads; completion is awaited by the s_waitcnt vmcnt(0) before the next
-// workgroup barrier.  M0 is saved and restored.
+// LDS reads; completion is awaited by an s_waitcnt vmcnt before the next workgroup
+// barrier.  M0 is saved and restored.  An SALU write of M0 needs one wait state
+// before an LDS-DMA load reads it (the compiler inserts it for its own copies, not
+// inside asm): without the s_nop the copy may land at the previous M0.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dwordx4 %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -73,6 +83,7 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
       "global_load_lds_dword %1, off\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -122,9 +133,10 @@ __device__ uint32_t compact(uint32_t (&skey)[kSlots], uint32_t (&spos)[kSlots], 
     return theta;
   }
   // radix select of the k-th largest 64-bit key, 8 bits at a time, most significant first
-  uint64_t prefix = 0, pmask = 0;
+  int shift = 56;
+  uint64_t pmask = 0ull, prefix = 0ull;
   uint32_t remaining = (uint32_t)k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (;; shift -= 8) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0u;
 #pragma unroll
@@ -166,7 +178,7 @@ __device__ uint32_t compact(uint32_t (&skey)[kSlots], uint32_t (&spos)[kSlots], 
     prefix |= (uint64_t)digit << shift;
     pmask |= (uint64_t)0xFFu << shift;
     remaining -= ab;
-    if (cnt == remaining) break;  // every key in this bin is selected
+    if (cnt == remaining || shift == 0) break;  // every key in this bin is selected
   }
   const uint64_t th = prefix;  // selected  <=>  key64 >= th  (exactly k keys)
 #pragma unroll
@@ -206,6 +218,7 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
                                                              int64_t n_keys, int32_t* __restrict__ idx_out,
                                                              float* __restrict__ score_out) {
   using C = FCfg<FP8, D>;
+  constexpr int kRing = ring_of<FP8, D>();
   __shared__ FusedSmem<FP8, D> sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
@@ -251,7 +264,12 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
   // ---- key tiles: copy j of a tile covers LDS bytes [1024 j, 1024 j + 1024); lane l
   // fills granule slot (l % gran) of row (1024 j / row_bytes + l / gran), holding the
   // row's granule slot ^ (row & 7) (XOR swizzle: conflict-free B-operand reads)
-  auto issue_tile = [&](int T, int bi) {
+  // Every wave issues the same number of copies per tile (kDmaPerWave), so the
+  // wait for tile T with later tiles in flight is a fixed vmcnt.
+  constexpr int kDmaPerWave = C::dma_per_tile / kFW + (FP8 ? 1 : 0);
+  static_assert(C::dma_per_tile % kFW == 0, "tile copies must spread evenly over the waves");
+  auto issue_tile = [&](int T) {
+    const int bi = T % kRing;
     for (int j = wave; j < C::dma_per_tile; j += kFW) {
       const int r = j * (1024 / C::row_bytes) + lane / C::gran;
       const int slot = lane % C::gran;
@@ -260,10 +278,26 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
       const uint8_t* src = kbytes + s * C::row_bytes + 16 * (slot ^ (r & 7));
       dma16(src, lds_u32(&sm.tile[bi][1024 * j]));
     }
-    if (FP8 && wave == kFW - 1) {
-      int64_t s = (int64_t)T * kFT + lane;
-      if (s > n_keys - 1) s = n_keys - 1;
-      dma4(kscale_g + s, lds_u32(&sm.kscale[bi][0]));
+    if constexpr (FP8) {
+      // wave w copies the scales of keys 8w .. 8w+7 of the tile (lanes 0-7 active)
+      if (lane < kFT / kFW) {
+        int64_t s = (int64_t)T * kFT + (kFT / kFW) * wave + lane;
+        if (s > n_keys - 1) s = n_keys - 1;
+        dma4(kscale_g + s, lds_u32(&sm.kscale[bi][(kFT / kFW) * wave]));
+      }
+    }
+  };
+  // s_waitcnt vmcnt(n) with the other counters unconstrained (n <= 15)
+  auto wait_vm = [&](int n) {
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+      case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+      case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+      case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+      case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+      case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+      case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+      default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
     }
   };
 
@@ -279,20 +313,24 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
   int n_pend = 0, n_state = 0;
   uint32_t theta = 0u;  // order keys of real scores are > 0: everything passes at first
 
-  issue_tile(0, 0);
+  for (int T = 0; T < kRing - 1 && T < n_tiles; ++T) issue_tile(T);
   for (int T = 0; T < n_tiles; ++T) {
-    const int bi = T & 1;
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies of tile T landed
-    __syncthreads();                     // ... and every wave's; buffer bi^1 is free
-    if (T + 1 < n_tiles) issue_tile(T + 1, bi ^ 1);
+    const int bi = T % kRing;
+    // this wave's copies of tile T landed (later tiles may still be in flight) ...
+    const int later = min(kRing - 2, n_tiles - 1 - T);
+    wait_vm(later * kDmaPerWave);
+    // ... and every wave's; tile T-1's buffer is no longer read.  LDS-only barrier:
+    // waits for this wave's LDS operations, not for the tiles still in flight; the
+    // "memory" clobber keeps the compiler from moving LDS accesses across it.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (T + kRing - 1 < n_tiles) issue_tile(T + kRing - 1);
     const uint8_t* tile = sm.tile[bi];
 
-    float part[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    // MFMAs of sub-block u+1 are issued before the ReLU-weighted head sum of
+    // sub-block u, so the VALU epilogue runs while the matrix core works.
+    auto mfma_sub = [&](int u, f32x4 (&acc)[HB]) {
       const int row = 16 * u + c;
       const uint8_t* rb = tile + row * C::row_bytes;
-      f32x4 acc[HB];
       if constexpr (FP8) {
         const i32x4 b0 = *reinterpret_cast<const i32x4*>(rb + 16 * ((2 * g) ^ (row & 7)));
         const i32x4 b1 = *reinterpret_cast<const i32x4*>(rb + 16 * ((2 * g + 1) ^ (row & 7)));
@@ -313,13 +351,30 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
           for (int hb = 0; hb < HB; ++hb) acc[hb] = mfma_bf16_16x16x32(qa[hb][ks], bf, acc[hb]);
         }
       }
-      float pv = 0.f;
+    };
+    // one accumulation chain per 16-head block (short dependency chains), then a tree
+    auto head_sum = [&](const f32x4 (&acc)[HB]) {
+      float ph[HB];
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb)
+      for (int hb = 0; hb < HB; ++hb) {
+        ph[hb] = wl[hb][0] * relu_bits(acc[hb][0]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv += wl[hb][r] * fmaxf(acc[hb][r], 0.f);
-      part[u] = pv;
-    }
+        for (int r = 1; r < 4; ++r) ph[hb] = fmaf(wl[hb][r], relu_bits(acc[hb][r]), ph[hb]);
+      }
+      if constexpr (HB == 4) return (ph[0] + ph[1]) + (ph[2] + ph[3]);
+      if constexpr (HB == 2) return ph[0] + ph[1];
+      return ph[0];
+    };
+    float part[4];
+    f32x4 accA[HB], accB[HB];
+    mfma_sub(0, accA);
+    mfma_sub(1, accB);
+    part[0] = head_sum(accA);
+    mfma_sub(2, accA);
+    part[1] = head_sum(accB);
+    mfma_sub(3, accB);
+    part[2] = head_sum(accA);
+    part[3] = head_sum(accB);
     // ---- finish the head sum: lane (g, c) -> key 16 g + c of the tile (= lane)
     const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
     const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
@@ -340,9 +395,18 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
       ppos[dst] = (uint32_t)s;
     }
     n_pend += (int)__popcll(m);
-    if (n_pend > kPendCap - kFT) {
-      theta = compact(skey, spos, pkey, ppos, hist, n_pend, n_state, theta, k, lane);
-      n_pend = 0;
+    // vote: compact every wave together (at the next tile) when any list is nearly
+    // full, so one wave's compaction does not hold the others at the barrier
+    // repeatedly.  Lists fill by at most kFT per tile, so one tile of delay is safe.
+    if (lane == 0) sm.need[T & 1][wave] = n_pend > kPendCap - 2 * kFT;
+    if (T > 0) {
+      int any = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kFW; ++w2) any |= sm.need[(T - 1) & 1][w2];
+      if (any && n_pend > 0) {
+        theta = compact(skey, spos, pkey, ppos, hist, n_pend, n_state, theta, k, lane);
+        n_pend = 0;
+      }
     }
   }
   if (n_pend > 0) theta = compact(skey, spos, pkey, ppos, hist, n_pend, n_state, theta, k, lane);

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16_16x16x32(a[hb][ks], bf[ks], acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part += wl[hb][r] * fmaxf(acc[r], 0.f);
+      for (int r = 0; r < 4; ++r) part += wl[hb][r] * relu_bits(acc[r]);
     }
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void idx_score_fp8_kernel(const uint8_t* __res
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = mfma_fp8_16x16x128(a[hb], bf, acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part += wl[hb][r] * fmaxf(acc[r], 0.f);
+      for (int r = 0; r < 4; ++r) part += wl[hb][r] * relu_bits(acc[r]);
     }
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
