@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all-f", action="store_true", help="skip the all-F comparison step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device twice (scale for the HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -98,12 +100,50 @@ def cpu_baseline(layers_host, roles, L, k, scale, seconds):
     return done / dt, done, dt, threads
 
 
+def traffic_record(kernel_file: str, kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None.
+
+    The summary (profiles/*_traffic.md) holds one JSON object per kernel and
+    workload: FETCH_SIZE + WRITE_SIZE per dispatch, scaled by the same counters'
+    reading for a plain copy of known size, and the sha256 of the kernel's source
+    file at the time of the counter runs.  A changed source voids the figure.
+    """
+    import glob
+    import hashlib
+    src = os.path.join(ROOT, "dsa_indexer_indexcache_amd", "csrc", kernel_file)
+    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_traffic.md"))):
+        for line in open(path):
+            line = line.strip()
+            if not line.startswith("{"):
+                continue
+            rec = json.loads(line)
+            if rec.get("kernel") == kernel and rec.get("workload") == workload and rec.get("source_sha256") == digest:
+                return rec
+    return None
+
+
+def copy_calibration(mib: int):
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 2}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
 
     import dsa_indexer_indexcache_amd as dsa
@@ -182,6 +222,11 @@ def main():
                 "unit": "TFLOP/s", "frac": dc["frac"], "traffic": None,
                 "avg_launch_ms": dc["ms_per_step"] / max(launches, 1),
                 "work_per_launch_tflop": (attn_flops if dom == "sparse_attn" else idx_flops) / max(launches, 1) / 1e12}
+    if dom == "sparse_attn" and args.L is None:
+        rec = traffic_record("sparse_attn.hip", "sparse_attn_pair_kernel", wl.name)
+        if rec is not None:
+            roofline["traffic"] = rec["hbm_bytes_per_launch"]
+            roofline["traffic_source"] = rec["summary"]
 
     extra = {}
     if not args.no_all_f and "S" in roles:
