@@ -35,7 +35,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--workload", type=int, default=4, help="synthetic workload id (4 = L=200K FSSS fp8)")
+    ap.add_argument("--workload", type=int, default=4,
+                    help="synthetic workload id (4 = L=200K FSSS fp8; 3 = decode B=8 over 47 layers)")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement after the prefill line")
     ap.add_argument("--L", type=int, default=None, help="override the context length (development only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all-f", action="store_true", help="skip the all-F comparison step")
@@ -135,6 +137,72 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 2}), flush=True)
 
 
+def run_decode(steps: int, warmup: int, hip, all_f: bool = True) -> dict:
+    """Decode step of the 47-layer stack: 8 sequences, one new query each, context
+    lengths drawn from [150000, 200000]; every layer's caches resident in HBM."""
+    import torch
+
+    import dsa_indexer_indexcache_amd as dsa
+    import synth
+
+    wid = 3
+    wl = synth.WORKLOADS[wid]
+    lens = synth.decode_lengths(wid)
+    seqs = dsa.Seqs.decode(lens)
+    roles, k, dev = wl.roles, wl.k, "cuda"
+    layers = [dsa.layer_dict(synth.decode_layer(l, lens, device=dev)) for l in range(len(roles))]
+    B, n_keys = len(lens), int(np.sum(lens))
+    outs = [torch.empty((B, wl.n_h, 512), dtype=torch.float32, device=dev) for _ in roles]
+    index_cache = torch.empty((B, k), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(rl, events=None):
+        return dsa.indexcache_forward(rl, layers, k, seqs=seqs, outs=outs, index_cache=index_cache, events=events)
+
+    def timed(rl):
+        for _ in range(warmup):
+            step(rl)
+        n_ev = 2 * (len(rl) + rl.count("F"))
+        evs = [hip.events(n_ev) for _ in range(steps)]
+        traces = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s_ in range(steps):
+            traces.append(step(rl, evs[s_]).trace)
+        torch.cuda.synchronize()
+        ms = 1e3 * (time.perf_counter() - t0) / steps
+        kind = {0: [], 1: []}
+        for s_, tr in enumerate(traces):
+            for j, (kd, _, _) in enumerate(tr):
+                kind[kd].append(hip.elapsed_ms(evs[s_][2 * j], evs[s_][2 * j + 1]))
+        return ms, kind
+
+    ms, kind = timed(roles)
+    n_f = roles.count("F")
+    idx_ms = float(np.mean(kind[0]))                     # one F layer: scores + selection
+    attn_ms = float(np.mean(kind[1]))                    # one layer's sparse attention
+    sel = int(np.sum(np.minimum(lens, k)))
+    idx_bytes = n_keys * (2 * wl.d + 4 + 4) + B * wl.H * (2 * wl.d + 2)   # keys, score write + read, q, w
+    attn_bytes = sel * 576 * 2 + B * wl.n_h * 576 * 2 + B * wl.n_h * 512 * 4 + B * k * 4
+    res = {"workload": wl.name, "lens": [int(x) for x in lens], "roles": roles,
+           "step_ms": ms, "steps": steps,
+           "indexer_topk_ms_per_F_layer": idx_ms, "indexer_calls_per_step": len(kind[0]) // steps,
+           "indexer_hbm_GBps": idx_bytes / (idx_ms * 1e-3) / 1e9,
+           "indexer_hbm_frac": idx_bytes / (idx_ms * 1e-3) / PEAK["hbm"],
+           "sparse_attn_ms_per_layer": attn_ms,
+           "sparse_attn_hbm_GBps": attn_bytes / (attn_ms * 1e-3) / 1e9,
+           "sparse_attn_hbm_frac": attn_bytes / (attn_ms * 1e-3) / PEAK["hbm"],
+           "indexer_bytes_per_F_layer": idx_bytes, "attn_bytes_per_layer": attn_bytes,
+           "indexer_work_saved": 1.0 - n_f / len(roles)}
+    if all_f:
+        ms_f, kind_f = timed("F" * len(roles))
+        res.update({"all_f_step_ms": ms_f, "step_speedup_pattern_vs_allF": ms_f / ms,
+                    "indexer_time_ratio_allF_over_pattern": float(np.sum(kind_f[0])) / float(np.sum(kind[0]))})
+    del layers, outs
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -150,7 +218,18 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.workload]
-    assert wl.decode_B == 0, "the bench times a prefill stack"
+    if wl.decode_B:
+        torch.cuda.init()
+        dsa.lib()
+        d = run_decode(args.steps, args.warmup, Hip(), all_f=not args.no_all_f)
+        print(json.dumps({
+            "metric": "decode step latency (47 layers, B=8, 150K-200K context)", "value": d["step_ms"],
+            "unit": "ms per decode step", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": d["step_ms"], "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16, fp32 accumulate", "data": "synthetic (seeded)",
+            "config": {"workload": wl.name, "B": wl.decode_B, "k": wl.k, "roles": wl.roles},
+            "decode": d}), flush=True)
+        return
     L = wl.L if args.L is None else args.L
     roles, k, dev = wl.roles, wl.k, "cuda"
     chunk = min(wl.q_chunk, L)
@@ -274,6 +353,12 @@ def main():
                "sample": "%d query rows drawn uniformly over [0, %d) through the %s stack (fp64 NumPy indexer, "
                          "sort top-k, sparse attention), %.1f s" % (nrows, L, roles, secs)}
 
+    dec = None
+    if not args.no_decode and args.L is None:
+        del layers, ldicts, outs, index_cache
+        torch.cuda.empty_cache()
+        dec = run_decode(max(args.steps, 3), 1, hip, all_f=not args.no_all_f)
+
     line = {
         "metric": "indexer+top-k queries/s & sparse-attn tok/s at L=200K; % MFMA/HBM peak",
         "value": L / (ms_step * 1e-3),
@@ -289,6 +374,7 @@ def main():
         "cpu_baseline": cpu,
     }
     line.update(extra)
+    line["decode"] = dec
     print(json.dumps(line), flush=True)
 
 
