@@ -67,8 +67,10 @@ dsa::IndexerArgs shape_args(int qk_dtype, int H, int d, int k, const dsa_seqs& s
 
 // The fused kernel needs no workspace; the slab path keeps one fp32 score per visible pair of a row.
 size_t indexer_ws(int64_t n_q, const dsa_seqs& s, int qk_dtype, int H, int d, int k) {
-  if (n_q == 0 || dsa::indexer_fused_ok(shape_args(qk_dtype, H, d, k, s))) return 0;
-  return (size_t)n_q * (size_t)dsa::slab_ld(s) * sizeof(float) + 256;
+  const dsa::IndexerArgs a = shape_args(qk_dtype, H, d, k, s);
+  if (n_q == 0 || dsa::indexer_fused_ok(a)) return 0;
+  const size_t slab = (size_t)n_q * (size_t)dsa::slab_ld(s) * sizeof(float) + 256;
+  return dsa::wide_select_ok(a) ? slab + dsa::wide_select_ws(a) : slab;
 }
 
 int check_indexer(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
@@ -135,7 +137,12 @@ int run_indexer(const dsa::IndexerArgs& a, void* ws, hipStream_t st) {
   float* slab = (float*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
   hipError_t e = dsa::launch_indexer_slab(a, slab, st);
   if (e != hipSuccess) return hip_fail(e, "indexer score launch");
-  e = dsa::launch_topk_select(a, slab, st);
+  if (dsa::wide_select_ok(a)) {
+    const int64_t n_q = a.seqs.q_start[a.seqs.B];
+    e = dsa::launch_wide_select(a, slab, slab + n_q * dsa::slab_ld(a.seqs), st);
+  } else {
+    e = dsa::launch_topk_select(a, slab, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "top-k select launch");
   return DSA_OK;
 }

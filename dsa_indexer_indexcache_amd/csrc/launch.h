@@ -36,6 +36,12 @@ int64_t slab_ld(const dsa_seqs& s);
 hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st);
 hipError_t launch_topk_select(const IndexerArgs& a, const float* slab, hipStream_t st);
 
+// topk_wide.hip: top-k of few long slab rows spread over (chunk, row) workgroups;
+// `state` is wide_select_ws() bytes of workspace.
+bool wide_select_ok(const IndexerArgs& a);
+size_t wide_select_ws(const IndexerArgs& a);
+hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* state, hipStream_t st);
+
 // indexer_fused.hip: one-sequence prefill, scores never leave the chip; no workspace.
 bool indexer_fused_ok(const IndexerArgs& a);
 hipError_t launch_indexer_fused(const IndexerArgs& a, hipStream_t st);

@@ -545,8 +545,10 @@ int attn_splits(const AttnArgs& a) {
   const int64_t n_q = a.seqs.q_start[a.seqs.B];
   const int nblk = (a.k + kBlk - 1) / kBlk;
   if (n_q >= 512 || nblk <= 1) return 1;
-  // spread few rows over enough workgroups to fill 256 CUs
-  int s = (int)((1024 + n_q - 1) / n_q);
+  // Spread few rows over about 128 workgroups.  Every split of a row writes an fp32
+  // partial of all heads (256 KB at 128 heads) that the combine pass reads back, so
+  // more splits than that cost more in partial traffic than they gain in occupancy.
+  int s = (int)((128 + n_q - 1) / n_q);
   if (s > nblk) s = nblk;
   if (s > 64) s = 64;
   return s < 1 ? 1 : s;

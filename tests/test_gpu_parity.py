@@ -173,6 +173,46 @@ def test_decode_varlen():
     check_attention(view, seqs, range(len(lens)), idx, out, 576 ** -0.5)
 
 
+def test_decode_wide_select_bf16():
+    """Few long rows: the (chunk, row) multi-workgroup select; one row shorter than k."""
+    announce("decode wide select bf16")
+    lens = [40000, 65537, 1000, 33000]
+    li = synth.make_layer(len(lens), sum(lens), 64, 128, 16, wid=3, layer=11, with_attention=False).to(DEV)
+    seqs = dsa.Seqs.decode(lens)
+    k = 2048
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, seqs, want_scores=True)
+    torch.cuda.synchronize()
+    print(check_indexer(OracleView(li), seqs, range(len(lens)), k, idx, sc, exact=False))
+
+
+def test_decode_wide_select_integer_exact():
+    """Integer-valued inputs (many equal scores): sets and scores bit-exact, ties to lower positions."""
+    announce("decode wide select integer")
+    lens = [50000, 36000, 2047]
+    li = synth.make_layer(len(lens), sum(lens), 8, 64, 16, wid=0, layer=5, integer_indexer=True,
+                          with_attention=False).to(DEV)
+    seqs = dsa.Seqs.decode(lens)
+    k = 2048
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, seqs, want_scores=True)
+    torch.cuda.synchronize()
+    check_indexer(OracleView(li), seqs, range(len(lens)), k, idx, sc, exact=True)
+
+
+def test_decode_wide_select_all_ties():
+    """Every score +-0: the threshold bin overflows the candidate list; the lowest positions win."""
+    announce("decode wide select all ties")
+    lens = [40000, 70001]
+    li = synth.make_layer(len(lens), sum(lens), 64, 128, 16, wid=3, layer=12, with_attention=False).to(DEV)
+    li.q_idx.zero_()
+    seqs = dsa.Seqs.decode(lens)
+    k = 2048
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, seqs, want_scores=True)
+    torch.cuda.synchronize()
+    want = torch.arange(k, dtype=torch.int32, device=DEV).expand(len(lens), k)
+    assert torch.equal(idx, want)
+    assert torch.all(sc == 0)
+
+
 # --------------------------------------------------------------------------- IndexCache loop
 
 def _stack(roles, L, k, wid=2, chunk=None, n_h=16):
