@@ -135,48 +135,68 @@ __device__ void find_bin(const uint32_t* gh, int k, int64_t n, int* d1_out, uint
 
 __global__ __launch_bounds__(kWThreads) void wsel_collect_kernel(const float* __restrict__ slab, int64_t ld,
                                                                   dsa_seqs seqs, int k, int mc, WideWs w) {
-  __shared__ uint32_t wsum[kWThreads / 64];
+  __shared__ uint32_t scan[kWThreads];
+  __shared__ uint32_t s_base;
   const int64_t i = blockIdx.y;
   const int c = blockIdx.x;
+  const int t = threadIdx.x;
   const int64_t n = row_len(seqs, i);
   const int64_t s0 = (int64_t)c * kWChunk;
   int d1;
   uint32_t above1;
   find_bin(w.hist + i * kWBins, k, n, &d1, &above1);
-  if (c == 0 && threadIdx.x == 0) {
+  if (c == 0 && t == 0) {
     w.meta[i].d1 = d1;
     w.meta[i].above1 = above1;
   }
+  // thread t owns keys s0 + 16t .. s0 + 16t + 15
   const float* row = slab + i * ld;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint32_t gt = 0;
+  uint32_t key[kWPer];
+  uint32_t gt = 0, nc = 0, candm = 0;
+#pragma unroll
   for (int j = 0; j < kWPer; ++j) {
-    const int64_t s = s0 + j * kWThreads + threadIdx.x;
+    const int64_t s = s0 + (int64_t)t * kWPer + j;
     const bool ok = s < n;
-    const uint32_t key = ok ? order_key(row[s]) : 0u;
-    const int bin = (int)(key >> kWShift1);
+    key[j] = ok ? order_key(row[s]) : 0u;
+    const int bin = (int)(key[j] >> kWShift1);
     gt += (ok && bin > d1) ? 1u : 0u;
     const bool cand = ok && bin == d1;
-    const uint64_t m = __ballot(cand);
-    if (m) {
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&w.meta[i].cand_cnt, (uint32_t)__popcll(m));
-      base = __shfl(base, 0);
-      if (cand) {
-        const uint32_t idx = base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-        if (idx < (uint32_t)kWCandCap) w.cand[i * kWCandCap + idx] = wkey64(key, (uint32_t)s);
+    nc += cand ? 1u : 0u;
+    candm |= (cand ? 1u : 0u) << j;
+  }
+  // candidate slots: exclusive scan of the per-thread counts, one reservation per
+  // workgroup (same-address atomics from every wave serialise at L2)
+  scan[t] = nc;
+  __syncthreads();
+  for (int d = 1; d < kWThreads; d <<= 1) {
+    const uint32_t o = t >= d ? scan[t - d] : 0u;
+    __syncthreads();
+    scan[t] += o;
+    __syncthreads();
+  }
+  if (t == kWThreads - 1) s_base = scan[t] ? atomicAdd(&w.meta[i].cand_cnt, scan[t]) : 0u;
+  uint32_t mine = scan[t] - nc;
+  __syncthreads();
+  const uint32_t base = s_base;
+  if (candm) {
+    uint32_t idx = base + mine;
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      if (candm >> j & 1u) {
+        if (idx < (uint32_t)kWCandCap)
+          w.cand[i * kWCandCap + idx] = wkey64(key[j], (uint32_t)(s0 + (int64_t)t * kWPer + j));
+        ++idx;
       }
     }
   }
   // chunk total of keys above the threshold bin
-  for (int d = 32; d >= 1; d >>= 1) gt += __shfl_xor(gt, d);
-  if (lane == 0) wsum[wv] = gt;
+  scan[t] = gt;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t tot = 0;
-    for (int q = 0; q < kWThreads / 64; ++q) tot += wsum[q];
-    w.gt[i * mc + c] = tot;
+  for (int d = kWThreads / 2; d >= 1; d >>= 1) {
+    if (t < d) scan[t] += scan[t + d];
+    __syncthreads();
   }
+  if (t == 0) w.gt[i * mc + c] = scan[0];
 }
 
 // Exact select inside the threshold bin; one workgroup per row.
