@@ -53,6 +53,41 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8&
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 64-lane global->LDS copy of 16 (or 4) bytes per lane to lds_base + lane * size,
+// issued from asm so that the compiler does not attach waits for it to unrelated
+// LDS reads; completion is awaited by an s_waitcnt vmcnt before the next workgroup
+// barrier.  M0 is saved and restored.  An SALU write of M0 needs one wait state
+// before an LDS-DMA load reads it (the compiler inserts it for its own copies, not
+// inside asm): without the s_nop the copy may land at the previous M0.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
 // Locate the sequence that owns packed query row i (wave-uniform; the table is
 // a kernel argument, so this is a short scalar loop).
 __device__ __forceinline__ int seq_of_row(const dsa_seqs& s, int64_t i) {

@@ -56,41 +56,6 @@ struct FusedSmem {
   int need[2][kFW];  // per-wave "pending list nearly full" votes, by tile parity
 };
 
-__device__ __forceinline__ uint32_t lds_u32(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// 64-lane global->LDS copy of 16 (or 4) bytes per lane to lds_base + lane * size,
-// issued from asm so that the compiler does not attach waits for it to unrelated
-// LDS reads; completion is awaited by an s_waitcnt vmcnt before the next workgroup
-// barrier.  M0 is saved and restored.  An SALU write of M0 needs one wait state
-// before an LDS-DMA load reads it (the compiler inserts it for its own copies, not
-// inside asm): without the s_nop the copy may land at the previous M0.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-      : "memory");
-}
-__device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-      : "memory");
-}
-
 __device__ __forceinline__ uint64_t key64(uint32_t key, uint32_t pos) {
   return ((uint64_t)key << 32) | (uint64_t)(0xFFFFFFFFu - pos);
 }

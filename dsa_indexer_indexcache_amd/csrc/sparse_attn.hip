@@ -20,6 +20,8 @@
 //   PV      : O[head][v] += P . V with P (bf16) as the A operand straight from the
 //             QK registers and V^T rows from LDS as the B operand; the key order
 //             inside the MFMA's K slots is the same permutation for both operands.
+#include <type_traits>
+
 #include "dsa_device.h"
 #include "launch.h"
 
@@ -271,19 +273,29 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Four LDS transpose reads (4 x b16 each) and the wait for them, in one asm
-// block: the compiler cannot tell these reads from the buffer being filled by
-// the asynchronous gather and would otherwise wait for that gather first.
-__device__ __forceinline__ void tr16_x4(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, uint64_t& d0,
-                                        uint64_t& d1, uint64_t& d2, uint64_t& d3) {
+// Four LDS transpose reads (4 x b16 each) at two bases and two immediate offsets,
+// and the wait for them, in one asm block: the compiler cannot tell these reads
+// from the buffer being filled by the asynchronous gather and would otherwise
+// wait for that gather first.
+template <int OFF>
+__device__ __forceinline__ void tr16_x4(uint32_t a0, uint32_t a1, uint64_t& d0, uint64_t& d1, uint64_t& d2,
+                                        uint64_t& d3) {
   asm volatile(
-      "ds_read_b64_tr_b16 %0, %4\n\t"
-      "ds_read_b64_tr_b16 %1, %5\n\t"
-      "ds_read_b64_tr_b16 %2, %6\n\t"
-      "ds_read_b64_tr_b16 %3, %7\n\t"
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
-      : "v"(a0), "v"(a1), "v"(a2), "v"(a3));
+      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 2048));
+}
+
+// max over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48), all lanes get it
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ __forceinline__ i32x4 pack_tr(uint64_t lo, uint64_t hi) {
@@ -294,7 +306,7 @@ __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
   return (uint32_t)((chunk >> 3) * (kBlk * 128) + row * 128 + 16 * ((chunk & 7) ^ (row & 7)));
 }
 
-template <int HG>
+template <int HG, int NW>
 __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ latent,
                                                                const int32_t* __restrict__ idx, int n_h, int k,
@@ -304,7 +316,7 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
                                                                float* __restrict__ part_o, float* __restrict__ part_ml) {
   __shared__ PairSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nwaves = blockDim.x >> 6;
+  constexpr int nwaves = NW;
   const int pair = wave >> 1, vh = wave & 1;
   const int64_t i = blockIdx.x / splits;
   const int split = blockIdx.x % splits;
@@ -418,8 +430,7 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
           x[kt][r] = okr[kt][r] ? st[hg][kt][r] * scale_log2 : -INFINITY;
           bmax = fmaxf(bmax, x[kt][r]);
         }
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      bmax = max_over_rows(bmax);
       if (__any(bmax > m[hg] + kLazy)) {
         const float mnew = fmaxf(m[hg], bmax);
         const float alpha = (m[hg] == -INFINITY) ? 0.f : exp2f(m[hg] - mnew);
@@ -434,8 +445,9 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
           for (int r = 0; r < 4; ++r) o[hg][vt][r] *= ar[r];
       }
       // p = 2^(x - m) (x = -inf gives 0), rounded once to bf16 pairs; the
-      // normaliser sums the rounded values
+      // normaliser sums the rounded values (a bf16 dot product with ones)
       const float mu = (m[hg] == -INFINITY) ? 0.f : m[hg];
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       float psum = 0.f;
       uint32_t pk[4];
 #pragma unroll
@@ -444,7 +456,7 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
         const bf16x2 v = {(__bf16)__builtin_amdgcn_exp2f(x[kt][r] - mu),
                           (__bf16)__builtin_amdgcn_exp2f(x[kt][r + 1] - mu)};
         pk[e] = __builtin_bit_cast(uint32_t, v);
-        psum += __uint_as_float(pk[e] << 16) + __uint_as_float(pk[e] & 0xFFFF0000u);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(v, ones, psum, false);
       }
       l[hg] += psum;
       pf[hg] = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
@@ -458,19 +470,26 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
     const uint8_t* vb0 = tile + r0 * 128 + 16 * ((2 * vh + (ta >> 1)) ^ (r0 & 7)) + 8 * (ta & 1);
     const uint8_t* vb1 = tile + r0 * 128 + 16 * ((4 + 2 * vh + (ta >> 1)) ^ (r0 & 7)) + 8 * (ta & 1);
     const uint32_t va0 = lds_addr(vb0), va1 = lds_addr(vb1);
-#pragma unroll
-    for (int vt = 0; vt < 16; vt += 2) {
-      // tiles vt (even: base 0) and vt + 1 (odd: base 1) share column group vt / 2
-      const uint32_t cgo = (vt >> 1) * (kBlk * 128);
+    // tiles vt (even: base 0) and vt + 1 (odd: base 1) share column group vt / 2
+    auto pv = [&](auto cg) {
+      constexpr int vt = 2 * decltype(cg)::value;
       uint64_t e0, e1, d0, d1;
-      tr16_x4(va0 + cgo, va0 + cgo + 2048, va1 + cgo, va1 + cgo + 2048, e0, e1, d0, d1);
+      tr16_x4<decltype(cg)::value * kBlk * 128>(va0, va1, e0, e1, d0, d1);
       const i32x4 vfe = pack_tr(e0, e1), vfo = pack_tr(d0, d1);
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
         o[hg][vt] = mfma_bf16_16x16x32(pf[hg], vfe, o[hg][vt]);
         o[hg][vt + 1] = mfma_bf16_16x16x32(pf[hg], vfo, o[hg][vt + 1]);
       }
-    }
+    };
+    pv(std::integral_constant<int, 0>{});
+    pv(std::integral_constant<int, 1>{});
+    pv(std::integral_constant<int, 2>{});
+    pv(std::integral_constant<int, 3>{});
+    pv(std::integral_constant<int, 4>{});
+    pv(std::integral_constant<int, 5>{});
+    pv(std::integral_constant<int, 6>{});
+    pv(std::integral_constant<int, 7>{});
   }
 
   // ---- finish
@@ -575,11 +594,20 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
     part_ml = part_o + (size_t)n_q * splits * a.n_h * kDv;
   }
   dim3 grid((unsigned)(n_q * splits));
-  if (a.n_h % 32 == 0 && a.k <= kIdxMax) {
-    // wave pairs of 32 heads: 2 * n_h / 32 waves
-    hipLaunchKernelGGL(sparse_attn_pair_kernel<2>, grid, dim3(64 * (a.n_h / 16)), 0, st, a.q, a.latent, a.idx,
-                       a.n_h, a.k, scale_log2, a.seqs, n_q, splits, splits == 1 ? out_f32 : nullptr,
-                       splits == 1 ? out_bf16 : nullptr, part_o, part_ml);
+  const bool paired = (a.n_h == 32 || a.n_h == 64 || a.n_h == 128) && a.k <= kIdxMax;
+  if (paired) {
+    // wave pairs of 32 heads: n_h / 16 waves
+#define DSA_PAIR(NWv)                                                                                            \
+  hipLaunchKernelGGL((sparse_attn_pair_kernel<2, NWv>), grid, dim3(64 * NWv), 0, st, a.q, a.latent, a.idx, a.n_h, \
+                     a.k, scale_log2, a.seqs, n_q, splits, splits == 1 ? out_f32 : nullptr,                        \
+                     splits == 1 ? out_bf16 : nullptr, part_o, part_ml)
+    if (a.n_h == 32)
+      DSA_PAIR(2);
+    else if (a.n_h == 64)
+      DSA_PAIR(4);
+    else
+      DSA_PAIR(8);
+#undef DSA_PAIR
   } else {
     // 16 heads per wave: the Q slice (72 VGPRs) and the O accumulator (128) stay
     // resident with two waves per SIMD and no spills.
