@@ -367,20 +367,39 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
   // 8(j%4) + l/8 at swizzled position l%8, i.e. it fetches granule (l%8) ^ (row & 7)
   const int lrow = lane >> 3, lpos = lane & 7;
   auto gather = [&](int blk, int bi) {
-    for (int j = wave; j < kTileIns; j += nwaves) {
-      const int r = 8 * (j & 3) + lrow;
-      const int chunk = 8 * (j >> 2) + (lpos ^ (r & 7));
+    if constexpr (NW % 4 == 0) {
+      // copies j = wave + NW m all fill rows 8 (wave % 4) .. +8: one index read, one
+      // address; copy m starts NW/4 column groups (16 NW elements) further along the row
+      const int r = 8 * (wave & 3) + lrow;
       const int s = sm.idx[blk * kBlk + r];
-      const uint16_t* src = lat + (int64_t)(s >= 0 ? s : 0) * kDqk + 8 * chunk;
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&sm.tile[bi][1024 * j], 16, 0,
-                                       0);
+      const uint16_t* src0 = lat + (int64_t)(s >= 0 ? s : 0) * kDqk + 8 * (8 * (wave >> 2) + (lpos ^ (r & 7)));
+      uint8_t* dst0 = &sm.tile[bi][1024 * wave];
+#pragma unroll
+      for (int m_ = 0; m_ < (kTileIns + NW - 1) / NW; ++m_) {
+        if (kTileIns % NW == 0 || wave + NW * m_ < kTileIns)
+          __builtin_amdgcn_global_load_lds(src0 + 16 * NW * m_,
+                                           (__attribute__((address_space(3))) void*)(dst0 + 1024 * NW * m_), 16, 0, 0);
+      }
+    } else {
+      for (int j = wave; j < kTileIns; j += nwaves) {
+        const int r = 8 * (j & 3) + lrow;
+        const int chunk = 8 * (j >> 2) + (lpos ^ (r & 7));
+        const int s = sm.idx[blk * kBlk + r];
+        const uint16_t* src = lat + (int64_t)(s >= 0 ? s : 0) * kDqk + 8 * chunk;
+        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&sm.tile[bi][1024 * j], 16,
+                                         0, 0);
+      }
     }
   };
 
   if (blk_lo < blk_hi) gather(blk_lo, 0);
   for (int blk = blk_lo; blk < blk_hi; ++blk) {
     const int bi = (blk - blk_lo) & 1;
-    __syncthreads();  // block blk landed for every wave; buffer bi^1 is free again
+    // This wave's copies of block blk landed (an explicit wait: the compiler does not
+    // reliably wait for direct-to-LDS copies at a barrier); after the barrier every
+    // wave's have, and buffer bi^1 (block blk-1) is no longer read.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
     if (blk + 1 < blk_hi) gather(blk + 1, bi ^ 1);
     const uint8_t* tile = sm.tile[bi];
 
