@@ -5,8 +5,9 @@
 // ([IDX] §2 TopK; §6.5 deterministic), without ever writing the score matrix.
 //
 // Workgroup: 8 waves, one query row per wave (8 consecutive rows), heaviest rows
-// first.  Keys stream through LDS in tiles of 64 (direct global->LDS copies, one
-// tile ahead); every wave scores its query against the tile:
+// first.  Keys stream through LDS in tiles of 128 (fp8) or 64 (bf16) keys by direct
+// global->LDS copies issued tiles ahead, one workgroup barrier per tile; every wave
+// scores its query against each 64-key sub-tile:
 //   MFMA   rows = 16 indexer heads, columns = 16 keys, K = head dim (fp8: one
 //          v_mfma_f32_16x16x128_f8f6f4 per 16x16 tile; bf16: d/32 x 16x16x32);
 //   head sum: lane (g, c) holds heads 4g+r of key c; it folds ReLU and w in
@@ -27,29 +28,34 @@ namespace dsa {
 
 namespace {
 
-constexpr int kFT = 64;         // keys per tile
+constexpr int kFT = 64;         // keys per sub-tile (one score per lane)
 constexpr int kFW = 8;          // waves (= query rows) per workgroup
 constexpr int kSlots = 32;      // state slots per lane: 2048 per wave
 constexpr int kPendCap = 1536;  // pending candidates per wave
 
+// Keys per tile (between workgroup barriers) = kFT x tm: fp8 key rows are small
+// enough for 128-key tiles, which halves the barriers per key.
 template <bool FP8, int D>
 struct FCfg {
+  static constexpr int tm = FP8 ? 2 : 1;                      // sub-tiles per tile
+  static constexpr int tile_keys = kFT * tm;
   static constexpr int row_bytes = FP8 ? D : 2 * D;           // one key row in LDS
-  static constexpr int tile_bytes = kFT * row_bytes;
+  static constexpr int tile_bytes = tile_keys * row_bytes;
   static constexpr int dma_per_tile = tile_bytes / 1024;     // 64 lanes x 16 B copies
   static constexpr int gran = row_bytes / 16;
 };
 
-// key tiles in LDS (the one being scored + ring-1 in flight): 4 small fp8 tiles or 2 bf16 tiles
+// key tiles in LDS (the one being scored + ring-1 in flight): 3 fp8 tiles of 16 KB,
+// 2 bf16 tiles of 16 KB (d = 128) or 4 of 8 KB (d = 64)
 template <bool FP8, int D>
 constexpr int ring_of() {
-  return FCfg<FP8, D>::tile_bytes <= 8192 ? 4 : 2;
+  return FP8 ? 3 : FCfg<FP8, D>::tile_bytes <= 8192 ? 4 : 2;
 }
 
 template <bool FP8, int D>
 struct FusedSmem {
   uint8_t tile[ring_of<FP8, D>()][FCfg<FP8, D>::tile_bytes];
-  float kscale[ring_of<FP8, D>()][kFT];
+  float kscale[ring_of<FP8, D>()][FCfg<FP8, D>::tile_keys];
   uint32_t pkey[kFW][kPendCap];
   uint32_t ppos[kFW][kPendCap];
   uint32_t hist[kFW][256];
@@ -194,7 +200,8 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
   const bool row_ok = i < n_q;
   const int64_t t = row_ok ? q_pos0 + i : -1;                         // this wave's position
   const int64_t t_max = q_pos0 + (i0 + kFW - 1 < n_q ? i0 + kFW - 1 : n_q - 1);
-  const int n_tiles = (int)((t_max + kFT) / kFT);
+  constexpr int kTK = FCfg<FP8, D>::tile_keys;
+  const int n_tiles = (int)((t_max + kTK) / kTK);
   const uint8_t* kbytes = (const uint8_t*)k_idx + k_row0 * C::row_bytes;
   const float* kscale_g = FP8 ? k_scale + k_row0 : nullptr;
 
@@ -238,17 +245,17 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
     for (int j = wave; j < C::dma_per_tile; j += kFW) {
       const int r = j * (1024 / C::row_bytes) + lane / C::gran;
       const int slot = lane % C::gran;
-      int64_t s = (int64_t)T * kFT + r;
+      int64_t s = (int64_t)T * kTK + r;
       if (s > n_keys - 1) s = n_keys - 1;  // tail rows past the keys: in-bounds, masked later
       const uint8_t* src = kbytes + s * C::row_bytes + 16 * (slot ^ (r & 7));
       dma16(src, lds_u32(&sm.tile[bi][1024 * j]));
     }
     if constexpr (FP8) {
-      // wave w copies the scales of keys 8w .. 8w+7 of the tile (lanes 0-7 active)
-      if (lane < kFT / kFW) {
-        int64_t s = (int64_t)T * kFT + (kFT / kFW) * wave + lane;
+      // wave w copies the scales of keys (kTK/8) w .. of the tile (kTK/8 lanes active)
+      if (lane < kTK / kFW) {
+        int64_t s = (int64_t)T * kTK + (kTK / kFW) * wave + lane;
         if (s > n_keys - 1) s = n_keys - 1;
-        dma4(kscale_g + s, lds_u32(&sm.kscale[bi][(kFT / kFW) * wave]));
+        dma4(kscale_g + s, lds_u32(&sm.kscale[bi][(kTK / kFW) * wave]));
       }
     }
   };
@@ -289,7 +296,9 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
     // "memory" clobber keeps the compiler from moving LDS accesses across it.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (T + kRing - 1 < n_tiles) issue_tile(T + kRing - 1);
-    const uint8_t* tile = sm.tile[bi];
+#pragma unroll
+    for (int sub = 0; sub < C::tm; ++sub) {
+    const uint8_t* tile = sm.tile[bi] + sub * kFT * C::row_bytes;
 
     // MFMAs of sub-block u+1 are issued before the ReLU-weighted head sum of
     // sub-block u, so the VALU epilogue runs while the matrix core works.
@@ -347,10 +356,10 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
     const float s13 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
     const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
     float score = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-    if constexpr (FP8) score *= sm.kscale[bi][lane];
+    if constexpr (FP8) score *= sm.kscale[bi][kFT * sub + lane];
 
     // ---- filter into the pending list
-    const int64_t s = (int64_t)T * kFT + lane;
+    const int64_t s = (int64_t)T * kTK + kFT * sub + lane;
     const uint32_t key = order_key(score);
     const bool pass = s <= t && key > theta;
     const uint64_t m = __ballot(pass);
@@ -360,10 +369,11 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
       ppos[dst] = (uint32_t)s;
     }
     n_pend += (int)__popcll(m);
+    }
     // vote: compact every wave together (at the next tile) when any list is nearly
     // full, so one wave's compaction does not hold the others at the barrier
-    // repeatedly.  Lists fill by at most kFT per tile, so one tile of delay is safe.
-    if (lane == 0) sm.need[T & 1][wave] = n_pend > kPendCap - 2 * kFT;
+    // repeatedly.  Lists fill by at most kTK per tile, so one tile of delay is safe.
+    if (lane == 0) sm.need[T & 1][wave] = n_pend > kPendCap - 2 * kTK;
     if (T > 0) {
       int any = 0;
 #pragma unroll
