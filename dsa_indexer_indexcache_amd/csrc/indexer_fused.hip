@@ -5,7 +5,7 @@
 // ([IDX] §2 TopK; §6.5 deterministic), without ever writing the score matrix.
 //
 // Workgroup: 8 waves, one query row per wave (8 consecutive rows), heaviest rows
-// first.  Keys stream through LDS in tiles of 128 (fp8) or 64 (bf16) keys by direct
+// first.  Keys stream through LDS in tiles of 256 (fp8) or 64 (bf16) keys by direct
 // global->LDS copies issued tiles ahead, one workgroup barrier per tile; every wave
 // scores its query against each 64-key sub-tile:
 //   MFMA   rows = 16 indexer heads, columns = 16 keys, K = head dim (fp8: one
@@ -31,13 +31,13 @@ namespace {
 constexpr int kFT = 64;         // keys per sub-tile (one score per lane)
 constexpr int kFW = 8;          // waves (= query rows) per workgroup
 constexpr int kSlots = 32;      // state slots per lane: 2048 per wave
-constexpr int kPendCap = 1536;  // pending candidates per wave
+constexpr int kPendCap = 1344;  // pending candidates per wave (LDS: 158 KB in all for fp8)
 
 // Keys per tile (between workgroup barriers) = kFT x tm: fp8 key rows are small
-// enough for 128-key tiles, which halves the barriers per key.
+// enough for 256-key tiles, a quarter of the barriers per key of 64-key tiles.
 template <bool FP8, int D>
 struct FCfg {
-  static constexpr int tm = FP8 ? 2 : 1;                      // sub-tiles per tile
+  static constexpr int tm = FP8 ? 4 : 1;                      // sub-tiles per tile
   static constexpr int tile_keys = kFT * tm;
   static constexpr int row_bytes = FP8 ? D : 2 * D;           // one key row in LDS
   static constexpr int tile_bytes = tile_keys * row_bytes;
@@ -45,11 +45,11 @@ struct FCfg {
   static constexpr int gran = row_bytes / 16;
 };
 
-// key tiles in LDS (the one being scored + ring-1 in flight): 3 fp8 tiles of 16 KB,
+// key tiles in LDS (the one being scored + ring-1 in flight): 2 fp8 tiles of 32 KB,
 // 2 bf16 tiles of 16 KB (d = 128) or 4 of 8 KB (d = 64)
 template <bool FP8, int D>
 constexpr int ring_of() {
-  return FP8 ? 3 : FCfg<FP8, D>::tile_bytes <= 8192 ? 4 : 2;
+  return FP8 ? 2 : FCfg<FP8, D>::tile_bytes <= 8192 ? 4 : 2;
 }
 
 template <bool FP8, int D>
@@ -96,6 +96,7 @@ __device__ __forceinline__ void fill_free(uint32_t (&skey)[kSlots], uint32_t (&s
 
 // Keeps exactly the k best of state + pending and returns the new threshold key.
 // Wave-level; uses this wave's histogram and pending areas of LDS only.
+template <bool NARROW>
 __device__ uint32_t compact(uint32_t (&skey)[kSlots], uint32_t (&spos)[kSlots], uint32_t* pkey, uint32_t* ppos,
                            uint32_t* hist, int n_pend, int& n_state, uint32_t theta, int k, int lane) {
   if (n_state + n_pend <= k) {
@@ -103,11 +104,44 @@ __device__ uint32_t compact(uint32_t (&skey)[kSlots], uint32_t (&spos)[kSlots], 
     n_state += n_pend;
     return theta;
   }
-  // radix select of the k-th largest 64-bit key, 8 bits at a time, most significant first
+  // radix select of the k-th largest 64-bit key, 8 bits at a time, most significant
+  // first.  NARROW: start at the highest bit where the candidates differ (their min
+  // and max agree above it, so the passes above would put every key into one bin and
+  // every lane's histogram atomic onto one LDS address); used where registers allow.
   int shift = 56;
   uint64_t pmask = 0ull, prefix = 0ull;
+  if constexpr (NARROW) {
+    uint64_t lo = ~0ull, hi = 0ull;
+#pragma unroll
+    for (int j = 0; j < kSlots; ++j) {
+      if (skey[j] != 0u) {
+        const uint64_t kk = key64(skey[j], spos[j]);
+        lo = kk < lo ? kk : lo;
+        hi = kk > hi ? kk : hi;
+      }
+    }
+    for (int p = lane; p < n_pend; p += 64) {
+      const uint64_t kk = key64(pkey[p], ppos[p]);
+      lo = kk < lo ? kk : lo;
+      hi = kk > hi ? kk : hi;
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint64_t olo = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(lo >> 32), d) << 32) |
+                           (uint32_t)__shfl_xor((int)(uint32_t)lo, d);
+      const uint64_t ohi = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(hi >> 32), d) << 32) |
+                           (uint32_t)__shfl_xor((int)(uint32_t)hi, d);
+      lo = olo < lo ? olo : lo;
+      hi = ohi > hi ? ohi : hi;
+    }
+    const int top = 63 - __clzll((long long)(lo ^ hi));
+    shift = top >= 7 ? top - 7 : 0;
+    pmask = shift + 8 >= 64 ? 0ull : ~0ull << (shift + 8);
+    prefix = hi & pmask;
+  }
   uint32_t remaining = (uint32_t)k;
   for (;; shift -= 8) {
+    if (shift < 0) shift = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) hist[4 * lane + b] = 0u;
 #pragma unroll
@@ -379,12 +413,12 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
 #pragma unroll
       for (int w2 = 0; w2 < kFW; ++w2) any |= sm.need[(T - 1) & 1][w2];
       if (any && n_pend > 0) {
-        theta = compact(skey, spos, pkey, ppos, hist, n_pend, n_state, theta, k, lane);
+        theta = compact<FP8>(skey, spos, pkey, ppos, hist, n_pend, n_state, theta, k, lane);
         n_pend = 0;
       }
     }
   }
-  if (n_pend > 0) theta = compact(skey, spos, pkey, ppos, hist, n_pend, n_state, theta, k, lane);
+  if (n_pend > 0) theta = compact<FP8>(skey, spos, pkey, ppos, hist, n_pend, n_state, theta, k, lane);
   if (!row_ok) return;
 
   // ---- write the row (valid entries first, unordered; a row sort follows)
