@@ -57,18 +57,16 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
     }
   }
 
-  for (int sb = 0; sb < kScoreKeysPerWave / 16; ++sb) {
-    const int64_t sbase = s0 + 16 * sb;
-    if (sbase > p) break;
-    const int64_t s = sbase + c;
-    i32x4 bf[KS];
+  // 16 keys per step; the keys of step sb + 1 are loaded while step sb is scored.
+  // Rows past the visible prefix load row p (in bounds) and are not written.
+  const int nsb = (int)min<int64_t>(kScoreKeysPerWave / 16, (p - s0) / 16 + 1);
+  auto load = [&](int sb, i32x4 (&bf)[KS]) {
+    const int64_t s = min<int64_t>(s0 + 16 * sb + c, p);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (s <= p)
-        bf[ks] = *reinterpret_cast<const i32x4*>(k_idx + (krow0 + s) * D + 32 * ks + 8 * g);
-      else
-        bf[ks] = i32x4{0, 0, 0, 0};
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      bf[ks] = *reinterpret_cast<const i32x4*>(k_idx + (krow0 + s) * D + 32 * ks + 8 * g);
+  };
+  auto score = [&](int sb, const i32x4 (&bf)[KS]) {
     float part = 0.f;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
@@ -78,9 +76,22 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
 #pragma unroll
       for (int r = 0; r < 4; ++r) part += wl[hb][r] * relu_bits(acc[r]);
     }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
+    // sum over the four 16-lane rows (heads 4g + r) by two permlane swaps
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    part = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+    part = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    const int64_t s = s0 + 16 * sb + c;
     if (g == 0 && s <= p) slab[i * ld + s] = part;
+  };
+  i32x4 bfa[KS], bfb[KS];
+  load(0, bfa);
+  for (int sb = 0; sb < nsb; sb += 2) {
+    if (sb + 1 < nsb) load(sb + 1, bfb);
+    score(sb, bfa);
+    if (sb + 1 >= nsb) break;
+    if (sb + 2 < nsb) load(sb + 2, bfa);
+    score(sb + 1, bfb);
   }
 }
 
