@@ -227,10 +227,11 @@ def sparse_attn(q: torch.Tensor, latent: torch.Tensor, idx: torch.Tensor, seqs: 
 
 
 class ForwardResult:
-    def __init__(self, outs, index_cache, score_cache, stats: Stats):
+    def __init__(self, outs, index_cache, score_cache, stats: Stats, ws=None):
         self.outs = outs
         self.index_cache = index_cache
         self.score_cache = score_cache
+        self.ws = ws          # the workspace used; pass it back to reuse it
         self.n_indexer_calls = int(stats.n_indexer_calls)
         self.n_chunks = int(stats.n_chunks)
         self.src_layer = [int(stats.src_layer[i]) for i in range(stats.n_layers)]
@@ -287,7 +288,7 @@ def indexcache_forward(roles: str, layers: Sequence[dict], k: int, seqs: Optiona
     _check(L.indexcache_forward(roles.encode(), arr, ctypes.byref(shape), ctypes.byref(seqs), _ptr(index_cache),
                                 _ptr(score_cache), _ptr(ws), ws.numel() if ws is not None else 0, ctypes.byref(stats),
                                 _stream(stream)))
-    return ForwardResult(outs, index_cache, score_cache, stats)
+    return ForwardResult(outs, index_cache, score_cache, stats, ws)
 
 
 def layer_dict(li) -> dict:

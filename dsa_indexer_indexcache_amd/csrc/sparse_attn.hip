@@ -240,10 +240,11 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
 // through LDS, after which both waves hold identical scores and run the same
 // softmax.  PV is split over alternating 16-column value tiles (wave vh takes
 // tiles 2 vt + vh), so each wave's O accumulator is 16*HG x 256.
-// Latent rows are gathered with direct global->LDS loads (no registers), one
-// block ahead of the block being computed, into a row-major tile padded to 73
-// granules per row (conflict-free b128 reads across 16 rows); V is read back
-// column-wise with the LDS transpose read, so no transposed copy is written.
+// Latent rows are gathered with direct global->LDS copies issued from asm (no
+// registers), one block ahead of the block being computed, into a row-major tile;
+// the copies are awaited by an explicit vmcnt wait before the block barrier.  V is
+// read back column-wise with the LDS transpose read, so no transposed copy is
+// written.
 // ----------------------------------------------------------------------------
 // LDS tile of one block: 9 column groups of 128 bytes (8 granules of 16 B) x 32
 // rows; inside a row the 8 granules are XOR-swizzled by (row & 7), so 16 rows
@@ -269,25 +270,14 @@ struct PairSmem {
 // clobber keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+// LDS transpose read (4 x b16).  The gather into LDS is issued from asm, so the
+// compiler, which does not see it, schedules these reads with no wait for it.
+__device__ __forceinline__ v4i16 tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const __attribute__((address_space(3))) void*)p);
 }
-
-// Four LDS transpose reads (4 x b16 each) at two bases and two immediate offsets,
-// and the wait for them, in one asm block: the compiler cannot tell these reads
-// from the buffer being filled by the asynchronous gather and would otherwise
-// wait for that gather first.
-template <int OFF>
-__device__ __forceinline__ void tr16_x4(uint32_t a0, uint32_t a1, uint64_t& d0, uint64_t& d1, uint64_t& d2,
-                                        uint64_t& d3) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
-      "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
-      "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
-      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
-      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 2048));
+__device__ __forceinline__ i32x4 pack_tr4(v4i16 lo, v4i16 hi) {
+  const uint64_t a = __builtin_bit_cast(uint64_t, lo), b = __builtin_bit_cast(uint64_t, hi);
+  return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)(uint32_t)b, (int)(uint32_t)(b >> 32)};
 }
 
 // max over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48), all lanes get it
@@ -296,10 +286,6 @@ __device__ __forceinline__ float max_over_rows(float x) {
   x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ i32x4 pack_tr(uint64_t lo, uint64_t hi) {
-  return i32x4{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
 }
 
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
@@ -377,8 +363,7 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
 #pragma unroll
       for (int m_ = 0; m_ < (kTileIns + NW - 1) / NW; ++m_) {
         if (kTileIns % NW == 0 || wave + NW * m_ < kTileIns)
-          __builtin_amdgcn_global_load_lds(src0 + 16 * NW * m_,
-                                           (__attribute__((address_space(3))) void*)(dst0 + 1024 * NW * m_), 16, 0, 0);
+          dma16(src0 + 16 * NW * m_, lds_u32(dst0 + 1024 * NW * m_));
       }
     } else {
       for (int j = wave; j < kTileIns; j += nwaves) {
@@ -386,8 +371,7 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
         const int chunk = 8 * (j >> 2) + (lpos ^ (r & 7));
         const int s = sm.idx[blk * kBlk + r];
         const uint16_t* src = lat + (int64_t)(s >= 0 ? s : 0) * kDqk + 8 * chunk;
-        __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)&sm.tile[bi][1024 * j], 16,
-                                         0, 0);
+        dma16(src, lds_u32(&sm.tile[bi][1024 * j]));
       }
     }
   };
@@ -488,27 +472,18 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
     const int r0 = 4 * g + tj;
     const uint8_t* vb0 = tile + r0 * 128 + 16 * ((2 * vh + (ta >> 1)) ^ (r0 & 7)) + 8 * (ta & 1);
     const uint8_t* vb1 = tile + r0 * 128 + 16 * ((4 + 2 * vh + (ta >> 1)) ^ (r0 & 7)) + 8 * (ta & 1);
-    const uint32_t va0 = lds_addr(vb0), va1 = lds_addr(vb1);
     // tiles vt (even: base 0) and vt + 1 (odd: base 1) share column group vt / 2
-    auto pv = [&](auto cg) {
-      constexpr int vt = 2 * decltype(cg)::value;
-      uint64_t e0, e1, d0, d1;
-      tr16_x4<decltype(cg)::value * kBlk * 128>(va0, va1, e0, e1, d0, d1);
-      const i32x4 vfe = pack_tr(e0, e1), vfo = pack_tr(d0, d1);
+#pragma unroll
+    for (int vt = 0; vt < 16; vt += 2) {
+      const int cgo = (vt >> 1) * (kBlk * 128);
+      const i32x4 vfe = pack_tr4(tr16(vb0 + cgo), tr16(vb0 + cgo + 2048));
+      const i32x4 vfo = pack_tr4(tr16(vb1 + cgo), tr16(vb1 + cgo + 2048));
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
         o[hg][vt] = mfma_bf16_16x16x32(pf[hg], vfe, o[hg][vt]);
         o[hg][vt + 1] = mfma_bf16_16x16x32(pf[hg], vfo, o[hg][vt + 1]);
       }
-    };
-    pv(std::integral_constant<int, 0>{});
-    pv(std::integral_constant<int, 1>{});
-    pv(std::integral_constant<int, 2>{});
-    pv(std::integral_constant<int, 3>{});
-    pv(std::integral_constant<int, 4>{});
-    pv(std::integral_constant<int, 5>{});
-    pv(std::integral_constant<int, 6>{});
-    pv(std::integral_constant<int, 7>{});
+    }
   }
 
   // ---- finish

@@ -36,3 +36,68 @@ def test_fused_indexer_has_no_vgpr_spills(tmp_path):
             kernels[name] = int(m.group(1))
     assert len(kernels) == 9, kernels
     assert all(v == 0 for v in kernels.values()), kernels
+
+
+def _kernel_bodies(asm: str, name_part: str):
+    """Assembly text of every kernel whose mangled name contains name_part."""
+    out, cur = [], None
+    for line in asm.splitlines():
+        if cur is None:
+            if re.match(r"^_Z\S*:", line) and name_part in line:
+                cur = []
+        else:
+            cur.append(line)
+            if "s_endpgm" in line:
+                out.append(cur)
+                cur = None
+    return out
+
+
+def _scratch_reload_with_copies_in_flight(body):
+    """Inside every loop that issues direct-to-LDS copies, a scratch reload between a
+    copy and the next s_waitcnt vmcnt(0) would wait for all copies in flight (the
+    counter completes in order) and serialise them.  Returns the offending lines."""
+    bad = []
+    headers = [(i, l.split(":")[0]) for i, l in enumerate(body) if re.match(r"^\.LBB\S+:", l) and "Loop Header" in l]
+    for h, label in headers:
+        ends = [i for i, l in enumerate(body) if i > h and re.search(r"s_c?branch\w*\s+" + re.escape(label) + r"\b", l)]
+        if not ends:
+            continue
+        seg = body[h:max(ends) + 1]
+        if not any("global_load_lds" in l for l in seg):
+            continue
+        inflight = False
+        for l in seg:
+            if "global_load_lds" in l:
+                inflight = True
+            elif re.search(r"s_waitcnt\s+vmcnt\(0\)", l):
+                inflight = False
+            elif inflight and "scratch_load" in l:
+                bad.append(l.strip())
+    return bad
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("src,kernel", [("sparse_attn.hip", "sparse_attn_pair_kernel"),
+                                        ("indexer_fused.hip", "idx_topk_fused_kernel")])
+def test_no_spill_reload_while_lds_copies_are_in_flight(tmp_path, src, kernel):
+    path = os.path.join(HERE, "..", "dsa_indexer_indexcache_amd", "csrc", src)
+    out = tmp_path / "k.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "--cuda-device-only", "-S", path, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    bodies = _kernel_bodies(out.read_text(), kernel)
+    assert bodies, "no %s in the assembly" % kernel
+    for body in bodies:
+        assert not _scratch_reload_with_copies_in_flight(body)
+
+
+def test_reload_scanner_flags_a_reload_after_a_copy():
+    loop = [".LBB0_3:                                ; =>This Inner Loop Header: Depth=1",
+            "\ts_waitcnt vmcnt(0)", "\ts_barrier", "\tglobal_load_lds_dwordx4 v[2:3], off",
+            "\tv_mfma_f32_16x16x32_bf16 v[4:7], v[8:11], v[12:15], v[4:7]",
+            "\tscratch_load_dword v0, off, off offset:8", "\ts_cbranch_scc0 .LBB0_3"]
+    assert _scratch_reload_with_copies_in_flight(loop) == ["scratch_load_dword v0, off, off offset:8"]
+    ok = loop[:5] + ["\ts_waitcnt vmcnt(0)"] + loop[5:]
+    assert _scratch_reload_with_copies_in_flight(ok) == []
