@@ -330,15 +330,14 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
     // "memory" clobber keeps the compiler from moving LDS accesses across it.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (T + kRing - 1 < n_tiles) issue_tile(T + kRing - 1);
-#pragma unroll
-    for (int sub = 0; sub < C::tm; ++sub) {
-    const uint8_t* tile = sm.tile[bi] + sub * kFT * C::row_bytes;
-
-    // MFMAs of sub-block u+1 are issued before the ReLU-weighted head sum of
-    // sub-block u, so the VALU epilogue runs while the matrix core works.
-    auto mfma_sub = [&](int u, f32x4 (&acc)[HB]) {
-      const int row = 16 * u + c;
-      const uint8_t* rb = tile + row * C::row_bytes;
+    // One software pipeline over the tile's 4 tm sub-blocks of 16 keys: the MFMAs of
+    // sub-block q+2 are issued right after the ReLU-weighted head sum of sub-block q,
+    // so the head sums, the cross-lane reduction and the filter of one 64-key
+    // sub-tile run while the matrix core works on the next.
+    // sub-block q of the tile: 16 keys 16q .. 16q+15 (sub-tile q / 4)
+    auto mfma_sub = [&](int q, f32x4 (&acc)[HB]) {
+      const int row = 16 * (q & 3) + c;
+      const uint8_t* rb = sm.tile[bi] + (q >> 2) * kFT * C::row_bytes + row * C::row_bytes;
       if constexpr (FP8) {
         const i32x4 b0 = *reinterpret_cast<const i32x4*>(rb + 16 * ((2 * g) ^ (row & 7)));
         const i32x4 b1 = *reinterpret_cast<const i32x4*>(rb + 16 * ((2 * g + 1) ^ (row & 7)));
@@ -360,7 +359,6 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
         }
       }
     };
-    // one accumulation chain per 16-head block (short dependency chains), then a tree
     auto head_sum = [&](const f32x4 (&acc)[HB]) {
       float ph[HB];
 #pragma unroll
@@ -373,36 +371,39 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
       if constexpr (HB == 2) return ph[0] + ph[1];
       return ph[0];
     };
-    float part[4];
-    f32x4 accA[HB], accB[HB];
-    mfma_sub(0, accA);
-    mfma_sub(1, accB);
-    part[0] = head_sum(accA);
-    mfma_sub(2, accA);
-    part[1] = head_sum(accB);
-    mfma_sub(3, accB);
-    part[2] = head_sum(accA);
-    part[3] = head_sum(accB);
-    // ---- finish the head sum: lane (g, c) -> key 16 g + c of the tile (= lane)
-    const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
-    const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
-    const float s02 = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);
-    const float s13 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
-    const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
-    float score = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-    if constexpr (FP8) score *= sm.kscale[bi][kFT * sub + lane];
+    // ---- sub-tile sub: finish the head sum (lane (g, c) -> key 16 g + c of the
+    // sub-tile, i.e. key 64 sub + lane of the tile) and filter
+    auto finish = [&](int sub, const float (&part)[4]) {
+      const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+      const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+      const float s02 = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);
+      const float s13 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
+      const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
+      float score = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+      if constexpr (FP8) score *= sm.kscale[bi][kFT * sub + lane];
 
-    // ---- filter into the pending list
-    const int64_t s = (int64_t)T * kTK + kFT * sub + lane;
-    const uint32_t key = order_key(score);
-    const bool pass = s <= t && key > theta;
-    const uint64_t m = __ballot(pass);
-    if (pass) {
-      const int dst = n_pend + (int)__popcll(m & ((1ull << lane) - 1ull));
-      pkey[dst] = key;
-      ppos[dst] = (uint32_t)s;
-    }
-    n_pend += (int)__popcll(m);
+      // ---- filter into the pending list
+      const int64_t s = (int64_t)T * kTK + kFT * sub + lane;
+      const uint32_t key = order_key(score);
+      const bool pass = s <= t && key > theta;
+      const uint64_t m = __ballot(pass);
+      if (pass) {
+        const int dst = n_pend + (int)__popcll(m & ((1ull << lane) - 1ull));
+        pkey[dst] = key;
+        ppos[dst] = (uint32_t)s;
+      }
+      n_pend += (int)__popcll(m);
+    };
+    constexpr int NQ = 4 * C::tm;
+    f32x4 acc[2][HB];
+    float part[4];
+    mfma_sub(0, acc[0]);
+    mfma_sub(1, acc[1]);
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      part[q & 3] = head_sum(acc[q & 1]);
+      if (q + 2 < NQ) mfma_sub(q + 2, acc[q & 1]);
+      if ((q & 3) == 3) finish(q >> 2, part);
     }
     // vote: compact every wave together (at the next tile) when any list is nearly
     // full, so one wave's compaction does not hold the others at the barrier
