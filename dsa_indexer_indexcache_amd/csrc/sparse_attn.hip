@@ -524,10 +524,14 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
 }
 
 // Merge split partials: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L.
+// Merges the split partials of one (row, head): weights 2^(m_s - M) / L per split
+// (computed once per thread, kept in registers), then every thread streams two of the
+// 512 value columns over the splits.
 __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml, int n_h,
                                                                   int splits, int64_t n_q, float* __restrict__ out_f32,
                                                                   uint16_t* __restrict__ out_bf16) {
+  constexpr int kMaxSplits = 64;
   const int64_t rh = blockIdx.x;  // (row, head)
   const int64_t i = rh / n_h;
   const int h = (int)(rh % n_h);
@@ -535,22 +539,35 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const float* _
   float M = -INFINITY;
   for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((i * splits + s) * n_h + h) * 2]);
   float L = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float ms = part_ml[((i * splits + s) * n_h + h) * 2];
-    if (ms != -INFINITY) L += part_ml[((i * splits + s) * n_h + h) * 2 + 1] * exp2f(ms - M);
+  float wgt[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    wgt[s] = 0.f;
+    if (s < splits) {
+      const float ms = part_ml[((i * splits + s) * n_h + h) * 2];
+      wgt[s] = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      L += part_ml[((i * splits + s) * n_h + h) * 2 + 1] * wgt[s];
+    }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  for (int v = threadIdx.x; v < kDv; v += blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < splits; ++s) {
-      const float ms = part_ml[((i * splits + s) * n_h + h) * 2];
-      if (ms != -INFINITY) acc += part_o[((i * splits + s) * n_h + h) * kDv + v] * exp2f(ms - M);
+  const float* po = part_o + (i * splits * (int64_t)n_h + h) * kDv;
+  const int64_t sstride = (int64_t)n_h * kDv;
+  const int v = threadIdx.x;
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s) {
+    if (s < splits) {
+      acc0 = fmaf(po[s * sstride + v], wgt[s], acc0);
+      acc1 = fmaf(po[s * sstride + v + 256], wgt[s], acc1);
     }
-    const float val = acc * inv;
-    if (out_f32)
-      out_f32[(i * n_h + h) * kDv + v] = val;
-    else
-      out_bf16[(i * n_h + h) * kDv + v] = (uint16_t)f32_to_bf16_bits(val);
+  }
+  const int64_t o = (i * n_h + h) * kDv + v;
+  if (out_f32) {
+    out_f32[o] = acc0 * inv;
+    out_f32[o + 256] = acc1 * inv;
+  } else {
+    out_bf16[o] = (uint16_t)f32_to_bf16_bits(acc0 * inv);
+    out_bf16[o + 256] = (uint16_t)f32_to_bf16_bits(acc1 * inv);
   }
 }
 
