@@ -77,6 +77,31 @@ def test_fp8_indexer():
     print(check_indexer(OracleView(li), seqs, sample_rows(3000, 512, 96), 512, idx, sc, exact=False))
 
 
+@pytest.mark.parametrize("H", [16, 32])
+def test_fp8_indexer_fewer_heads(H):
+    """The fused fp8 kernel with one and two 16-head blocks."""
+    announce("fp8 indexer H=%d" % H)
+    li = layer(2100, H, 128, 16, wid=4, layer_id=3, dtype="fp8")
+    seqs = dsa.Seqs.prefill(2100)
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 300, seqs, q_scale=li.q_scale, k_scale=li.k_scale,
+                               want_scores=True)
+    torch.cuda.synchronize()
+    print(check_indexer(OracleView(li), seqs, sample_rows(2100, 300, 64), 300, idx, sc, exact=False))
+
+
+def test_fp8_decode_wide_select():
+    """fp8 decode: the fp8 score slab (per-row scales) and the chunked select."""
+    announce("fp8 decode")
+    lens = [40000, 33000, 500]
+    li = synth.make_layer(len(lens), sum(lens), 64, 128, 16, wid=4, layer=9, qk_dtype="fp8",
+                          with_attention=False).to(DEV)
+    seqs = dsa.Seqs.decode(lens)
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 2048, seqs, q_scale=li.q_scale, k_scale=li.k_scale,
+                               want_scores=True)
+    torch.cuda.synchronize()
+    print(check_indexer(OracleView(li), seqs, range(len(lens)), 2048, idx, sc, exact=False))
+
+
 def test_chunk_offsets_match_one_call():
     """Queries scored in chunks (q_pos0 > 0, full key prefix) give the same rows as one call."""
     announce("chunked indexer")
