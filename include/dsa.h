@@ -104,7 +104,7 @@ int dsa_indexer_topk(const void* q_idx, const float* q_scale, const void* k_idx,
  * prefill with at least 256 query rows, k <= 2048 and d in {64,128} (scores never
  * leave the chip); otherwise an fp32 score slab of n_q x (longest visible prefix)
  * plus, for at most 64 rows whose prefix reaches 32768 keys (decode), the state of
- * the chunked multi-workgroup select (about 128 KB per row). */
+ * the chunked multi-workgroup select (about 140 KB per row). */
 size_t dsa_indexer_topk_ws(int qk_dtype, int H, int d, int k, const dsa_seqs* seqs /* host */);
 
 /* ---------------------------------------------------------------- sparse attention */
