@@ -263,6 +263,7 @@ struct PairSmem {
   uint8_t tile[kNBuf][kTileBytes];
   f32x4 xs[kMaxWaves][4][64];   // partial score exchange, [wave][register quad][lane]
   int idx[kIdxMax];             // the row's selected positions (-1 = skip)
+  float bias[kIdxMax];          // 0 for a usable slot, -inf for a skipped one
 };
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
@@ -322,7 +323,9 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
   const int32_t* irow = idx + i * (int64_t)k;
   for (int j = tid; j < nblk_total * kBlk; j += blockDim.x) {
     const int32_t s = j < k ? irow[j] : -1;
-    sm.idx[j] = (s >= 0 && s <= p) ? s : -1;
+    const bool ok = s >= 0 && s <= p;
+    sm.idx[j] = ok ? s : -1;
+    sm.bias[j] = ok ? 0.f : -INFINITY;
   }
 
   // q slice: B operand of QK; lane -> head (16hg + c); this wave takes the 32-column
@@ -415,12 +418,11 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) st[hg][kt] += sm.xs[wave ^ 1][2 * hg + kt][lane];
 
-    // ---- online softmax (identical in both waves of the pair)
-    bool okr[2][4];
+    // ---- online softmax (identical in both waves of the pair); skipped slots get
+    // -inf through an additive bias
+    f32x4 bias[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) okr[kt][r] = sm.idx[blk * kBlk + 16 * kt + 4 * g + r] >= 0;
+    for (int kt = 0; kt < 2; ++kt) bias[kt] = *reinterpret_cast<const f32x4*>(&sm.bias[blk * kBlk + 16 * kt + 4 * g]);
     i32x4 pf[HG];
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          x[kt][r] = okr[kt][r] ? st[hg][kt][r] * scale_log2 : -INFINITY;
+          x[kt][r] = fmaf(st[hg][kt][r], scale_log2, bias[kt][r]);
           bmax = fmaxf(bmax, x[kt][r]);
         }
       bmax = max_over_rows(bmax);
