@@ -374,8 +374,10 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
     // ---- sub-tile sub: finish the head sum (lane (g, c) -> key 16 g + c of the
     // sub-tile, i.e. key 64 sub + lane of the tile) and filter
     auto finish = [&](int sub, const float (&part)[4]) {
-      const auto x02 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
-      const auto x13 = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
+      const auto x02 =
+          __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[2]), false, false);
+      const auto x13 =
+          __builtin_amdgcn_permlane32_swap(__float_as_uint(part[1]), __float_as_uint(part[3]), false, false);
       const float s02 = __uint_as_float(x02[0]) + __uint_as_float(x02[1]);
       const float s13 = __uint_as_float(x13[0]) + __uint_as_float(x13[1]);
       const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
