@@ -314,6 +314,24 @@ def main():
             roofline["traffic"] = rec["hbm_bytes_per_launch"]
             roofline["traffic_source"] = rec["summary"]
 
+    # cross-layer overlap diagnostic at the chunk shape: the step's index cache against
+    # a row-rotated copy of itself (reads 2 x rows x k x 4 B, writes 4 B per row)
+    other = torch.roll(index_cache, 1, dims=0).contiguous()
+    counts = dsa.index_overlap(index_cache, other)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dsa.index_overlap(index_cache, other, counts=counts)
+    e1.record()
+    torch.cuda.synchronize()
+    ov_ms = e0.elapsed_time(e1) / reps
+    ov_bytes = 2.0 * index_cache.numel() * 4 + index_cache.shape[0] * 4
+    overlap_line = {"rows": int(index_cache.shape[0]), "k": k, "us_per_launch": 1e3 * ov_ms,
+                    "hbm_GBps": ov_bytes / (ov_ms * 1e-3) / 1e9, "hbm_frac": ov_bytes / (ov_ms * 1e-3) / PEAK["hbm"]}
+    del other, counts
+
     extra = {}
     if not args.no_all_f and "S" in roles:
         allf = "F" * len(roles)
@@ -381,6 +399,7 @@ def main():
         "cpu_baseline": cpu,
     }
     line.update(extra)
+    line["index_overlap"] = overlap_line
     line["decode"] = dec
     print(json.dumps(line), flush=True)
 

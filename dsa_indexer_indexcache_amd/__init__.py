@@ -25,7 +25,7 @@ STATUS = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_ROLES", -3: "DSA_
 
 EXPORTS = ("dsa_indexer_topk", "dsa_indexer_topk_ws", "dsa_sparse_attn", "dsa_sparse_attn_ws",
            "indexcache_forward", "indexcache_forward_ws", "indexcache_plan", "dsa_status_string",
-           "dsa_last_error", "dsa_version")
+           "dsa_last_error", "dsa_version", "dsa_index_overlap")
 
 
 class DsaError(RuntimeError):
@@ -139,6 +139,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_last_error.restype = ctypes.c_char_p
         L.dsa_version.argtypes = []
         L.dsa_version.restype = i32
+        L.dsa_index_overlap.argtypes = [vp, vp, ctypes.c_int64, i32, vp, vp]
+        L.dsa_index_overlap.restype = i32
         _lib_handle = L
     return _lib_handle
 
@@ -224,6 +226,19 @@ def sparse_attn(q: torch.Tensor, latent: torch.Tensor, idx: torch.Tensor, seqs: 
     _check(L.dsa_sparse_attn(_ptr(q), _ptr(latent), _ptr(idx), n_h, d_qk, d_v, k, float(scale), ctypes.byref(seqs),
                              _ptr(out), odt, _ptr(ws), nbytes, _stream(stream)))
     return out
+
+
+def index_overlap(idx_a: torch.Tensor, idx_b: torch.Tensor, counts: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """dsa_index_overlap: counts[i] = |valid(idx_a[i]) ∩ valid(idx_b[i])| (int32); divide by k
+    for the overlap fraction."""
+    if idx_a.shape != idx_b.shape or idx_a.dim() != 2:
+        raise ValueError("two [n_rows, k] index tensors of one shape are needed")
+    n_rows, k = idx_a.shape
+    if counts is None:
+        counts = torch.empty((n_rows,), dtype=torch.int32, device=idx_a.device)
+    _check(lib().dsa_index_overlap(_ptr(idx_a), _ptr(idx_b), n_rows, k, _ptr(counts), _stream(stream)))
+    return counts
 
 
 class ForwardResult:

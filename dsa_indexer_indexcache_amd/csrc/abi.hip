@@ -195,7 +195,18 @@ size_t elt_size(int dtype) { return dtype == DSA_FP8_E4M3 ? 1 : dtype == DSA_BF1
 
 extern "C" {
 
-int dsa_version(void) { return 100; }
+int dsa_version(void) { return 101; }
+
+int dsa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int k, int32_t* counts,
+                      void* stream) {
+  if (n_rows < 0) return fail(DSA_ERR_INVALID_ARG, "n_rows=%lld < 0", (long long)n_rows);
+  if (k < 1 || k > dsa::kOverlapMaxK) return fail(DSA_ERR_UNSUPPORTED, "k=%d outside [1, %d]", k, dsa::kOverlapMaxK);
+  if (n_rows == 0) return DSA_OK;
+  if (!idx_a || !idx_b || !counts) return fail(DSA_ERR_INVALID_ARG, "null pointer");
+  hipError_t e = dsa::launch_index_overlap(idx_a, idx_b, n_rows, k, counts, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "index overlap launch");
+  return DSA_OK;
+}
 
 const char* dsa_status_string(int status) {
   switch (status) {

@@ -46,6 +46,11 @@ hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* sta
 bool indexer_fused_ok(const IndexerArgs& a);
 hipError_t launch_indexer_fused(const IndexerArgs& a, hipStream_t st);
 
+// diagnostics.hip: per-row intersection counts of two index tensors (k <= kOverlapMaxK).
+constexpr int kOverlapMaxK = 16384;
+hipError_t launch_index_overlap(const int32_t* a, const int32_t* b, int64_t n_rows, int k, int32_t* counts,
+                                hipStream_t st);
+
 // sparse_attn.hip
 int attn_splits(const AttnArgs& a);
 size_t attn_ws_bytes(const AttnArgs& a);

@@ -206,6 +206,20 @@ size_t indexcache_forward_ws(const char* roles, const dsa_shape* shape, const ds
  */
 int indexcache_plan(const char* roles, int32_t* src_layer, int32_t* n_indexer_calls);
 
+/* ---------------------------------------------------------------- diagnostics */
+/*
+ * Cross-layer index overlap ([IDX] §8 metrics: the share of one layer's selected
+ * set that another layer also selects; [IC] §1 motivates index reuse by this
+ * similarity between layers).  For every row i, counts[i] = |A_i ∩ B_i|, where A_i
+ * and B_i are the sets of valid (>= 0) entries of idx_a[i, :] and idx_b[i, :]
+ * (row order does not matter; valid entries of a row must be distinct, as the
+ * indexer writes them).  Overlap^(l,l') of the row = counts[i] / k.
+ *   idx_a, idx_b [n_rows, k] int32 (device);  counts [n_rows] int32 (device, written)
+ * 1 <= k <= 16384; n_rows == 0 is a no-op.  Exact (integer) result.
+ */
+int dsa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int k, int32_t* counts,
+                      void* stream);
+
 /* ---------------------------------------------------------------- misc */
 const char* dsa_status_string(int status); /* static string                         */
 const char* dsa_last_error(void);          /* thread-local detail of the last error */

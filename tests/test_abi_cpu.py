@@ -30,7 +30,7 @@ def test_exports_every_declared_symbol():
     L = dsa.lib()
     for n in names:
         assert hasattr(L, n)
-    assert L.dsa_version() == 100
+    assert L.dsa_version() == 101
 
 
 def test_status_strings():
@@ -150,3 +150,13 @@ def test_forward_validation():
     bad.out_rows, bad.n_h = 64, 20
     assert call(b"FS", shape=bad) == -4
     assert call(b"FS") == -6                                       # workspace 0 bytes
+
+
+def test_index_overlap_validation():
+    """Argument checks of dsa_index_overlap run before any launch (no GPU needed)."""
+    L = dsa.lib()
+    assert L.dsa_index_overlap(None, None, 0, 2048, None, None) == 0          # no rows: a no-op
+    assert L.dsa_index_overlap(None, None, 4, 0, None, None) == -4            # k < 1
+    assert L.dsa_index_overlap(None, None, 4, 16385, None, None) == -4        # k too large
+    assert L.dsa_index_overlap(None, None, -1, 16, None, None) == -1          # negative row count
+    assert L.dsa_index_overlap(None, None, 4, 16, None, None) == -1           # null pointers

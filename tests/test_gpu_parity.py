@@ -310,3 +310,50 @@ def test_attention_large_budget_fallback():
     out = dsa.sparse_attn(li.q, li.latent, idx_t, seqs)
     torch.cuda.synchronize()
     check_attention(OracleView(li), seqs, [0, 5, 2047, 2048, 2099, 2100, 2299], idx_t, out, 576 ** -0.5)
+
+
+# --------------------------------------------------------------------------- diagnostics
+
+def _overlap_rows(n, k, seed):
+    """Index rows with every overlap from none to all, shuffled order and -1 padding."""
+    g = np.random.default_rng(seed)
+    a = np.full((n, k), -1, dtype=np.int32)
+    b = np.full((n, k), -1, dtype=np.int32)
+    for i in range(n):
+        va = int(g.integers(0, k + 1))
+        vb = int(g.integers(0, k + 1))
+        pool = g.permutation(4 * k + 7)
+        common = int(g.integers(0, min(va, vb) + 1))
+        sa = pool[:va]
+        sb = np.concatenate([sa[:common], pool[va:va + vb - common]])
+        a[i, :va] = g.permutation(sa)
+        b[i, :vb] = g.permutation(sb)
+        a[i] = g.permutation(a[i])
+        b[i] = g.permutation(b[i])
+    return a, b
+
+
+@pytest.mark.parametrize("n,k", [(700, 2048), (300, 7), (40, 16384)])
+def test_index_overlap_exact(n, k):
+    announce("index overlap n=%d k=%d" % (n, k))
+    a, b = _overlap_rows(n, k, seed=k)
+    got = dsa.index_overlap(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV))
+    torch.cuda.synchronize()
+    want = np.array([round(oracle.overlap(a[i], b[i], k) * k) for i in range(n)], dtype=np.int32)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_index_overlap_between_two_f_layers():
+    """Cross-layer overlap of two F layers' own selections (FF stack), against the oracle."""
+    announce("index overlap of two F layers")
+    L, k = 1500, 128
+    layers = [synth.make_layer(L, L, 64, 128, 16, wid=2, layer=l).to(DEV) for l in range(2)]
+    seqs = dsa.Seqs.prefill(L)
+    i0, _ = dsa.indexer_topk(layers[0].q_idx, layers[0].k_idx, layers[0].w, k, seqs)
+    i1, _ = dsa.indexer_topk(layers[1].q_idx, layers[1].k_idx, layers[1].w, k, seqs)
+    got = dsa.index_overlap(i0, i1)
+    torch.cuda.synchronize()
+    a, b = i0.cpu().numpy(), i1.cpu().numpy()
+    want = np.array([round(oracle.overlap(a[i], b[i], k) * k) for i in range(L)], dtype=np.int32)
+    assert np.array_equal(got.cpu().numpy(), want)
+    assert got[:k].eq(torch.arange(1, k + 1, device=DEV, dtype=torch.int32)).all()   # t < k: all rows visible

@@ -351,3 +351,13 @@ def test_index_override_and_overlap_metric():
     r = indexcache_forward("FS", layers, list(range(L)), k, 1.0, 4, index_override={0: forced})
     np.testing.assert_array_equal(r["index"][1], forced)
     assert oracle.overlap([0, 1, -1], [1, 2, 0], 3) == 2 / 3
+
+
+def test_overlap_special_cases():
+    """Overlap = |A ∩ B| / k over valid entries: identical full rows give 1, disjoint rows 0,
+    order and -1 padding do not matter, and a short row (fewer than k valid) stays below 1."""
+    a = np.arange(8)
+    assert oracle.overlap(a, a[::-1], 8) == 1.0
+    assert oracle.overlap(a, a + 8, 8) == 0.0
+    assert oracle.overlap([3, 1, -1, -1], [1, -1, 3, -1], 4) == 0.5
+    assert oracle.overlap([0, 1, 2, -1], [2, 1, 0, -1], 4) == 0.75
