@@ -18,11 +18,11 @@ definitions on the source pages.  Citations use two page titles:
 Every function here is pinned by tests under tests/ against closed forms,
 hand-derived fixtures, brute force and library routines (see test_oracle_*.py).
 """
-from .formats import decode_bf16, decode_e4m3fn, e4m3fn_table, dequant_rows
+from .formats import decode_bf16, decode_e4m3fn, e4m3fn_table, dequant_rows, encode_e4m3fn, quantize_fp8_rows
 from .dsa import (indexer_row, indexer_row_int2, topk_row, attn_row, dense_attn_row,
                   indexcache_plan, indexcache_forward, RoleError, tolerance_row,
                   captured_mass, overlap)
 
-__all__ = ["decode_bf16", "decode_e4m3fn", "e4m3fn_table", "dequant_rows", "indexer_row",
+__all__ = ["decode_bf16", "decode_e4m3fn", "e4m3fn_table", "dequant_rows", "encode_e4m3fn", "quantize_fp8_rows", "indexer_row",
            "indexer_row_int2", "topk_row", "attn_row", "dense_attn_row", "indexcache_plan",
            "indexcache_forward", "RoleError", "tolerance_row", "captured_mass", "overlap"]

@@ -56,3 +56,36 @@ def dequant_rows(payload: np.ndarray, scale, dtype: str) -> np.ndarray:
         s = np.asarray(scale, dtype=np.float32).astype(np.float64)
         return v * s[..., None]
     raise ValueError(dtype)
+
+
+def encode_e4m3fn(y) -> np.ndarray:
+    """Finite float values with |y| <= 448 -> OCP e4m3fn codes, round to nearest, ties
+    to the even mantissa; the sign is kept (-0.0 and negatives that round to zero give
+    0x80).  Written from the format definition: the nearest of the 127 finite
+    non-negative magnitudes (codes 0x00 .. 0x7E), by exhaustive comparison."""
+    y = np.asarray(y, dtype=np.float64)
+    assert np.all(np.isfinite(y)) and np.all(np.abs(y) <= 448.0)
+    mags = _E4M3[:0x7F]                       # increasing in the code
+    a = np.abs(y)[..., None]
+    d = np.abs(a - mags)                      # distance to every magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best                          # one code, or two at a tie
+    codes = np.arange(0x7F)
+    even = (codes & 1) == 0
+    pick = np.where(cand & even, codes, 0x7F).min(axis=-1)        # tie: the even mantissa
+    single = np.where(cand, codes, 0x7F).min(axis=-1)
+    code = np.where(cand.sum(axis=-1) > 1, pick, single).astype(np.uint8)
+    neg = np.signbit(y)
+    return np.where(neg, code | 0x80, code).astype(np.uint8)
+
+
+def quantize_fp8_rows(x: np.ndarray):
+    """Per-row quantisation of the indexer inputs, in fp32 arithmetic (the precision
+    that takes the rounding decision): scale = amax/448 over the row (1 for an all-zero
+    row), y = clamp(x / scale, +-448), codes = encode_e4m3fn(y).  Returns (codes uint8,
+    scales float32)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.abs(x).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = np.clip(x / scale[..., None], np.float32(-448.0), np.float32(448.0)).astype(np.float32)
+    return encode_e4m3fn(y), scale

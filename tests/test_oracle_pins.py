@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import oracle
+import synth
 from oracle import (attn_row, decode_bf16, decode_e4m3fn, dense_attn_row, indexcache_forward,
                     indexcache_plan, indexer_row, indexer_row_int2, topk_row, RoleError)
 
@@ -361,3 +362,43 @@ def test_overlap_special_cases():
     assert oracle.overlap(a, a + 8, 8) == 0.0
     assert oracle.overlap([3, 1, -1, -1], [1, -1, 3, -1], 4) == 0.5
     assert oracle.overlap([0, 1, 2, -1], [2, 1, 0, -1], 4) == 0.75
+
+
+def test_e4m3fn_encoder_round_trip_and_hand_values():
+    """Every finite code decodes and re-encodes to itself (signed zero included); values
+    worked out by hand from the format: the maximum, a power of two, ties to the even
+    mantissa in the normal and subnormal ranges, and signed zero."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.decode_e4m3fn(codes)
+    ok = ~np.isnan(vals)
+    assert np.array_equal(oracle.encode_e4m3fn(vals[ok]), codes[ok])
+    cases = [(448.0, 0x7E), (-448.0, 0xFE), (0.5, 0x30), (1.0625, 0x38), (1.1875, 0x3A), (2.0 ** -9, 0x01),
+             (2.0 ** -10, 0x00), (3 * 2.0 ** -10, 0x02), (-0.0, 0x80), (0.0, 0x00), (440.0, 0x7E)]
+    for v, c in cases:
+        assert int(oracle.encode_e4m3fn(v)) == c, (v, c)
+
+
+def test_e4m3fn_encoder_matches_torch_cast():
+    """An independent implementation: torch's CPU float8_e4m3fn cast (round to nearest
+    even) on values spread over the whole range, subnormals included."""
+    g = np.random.default_rng(5)
+    v = (g.standard_normal(20000) * np.exp2(g.integers(-12, 9, 20000))).astype(np.float32)
+    v = np.clip(v, -448, 448)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.encode_e4m3fn(v), want)
+
+
+def test_quantize_rows_definition():
+    """Zero rows get scale 1 and zero codes; each row's largest magnitude lands on +-448;
+    the result equals the seeded generators' torch-based quantiser."""
+    g = np.random.default_rng(6)
+    x = (g.standard_normal((64, 128)) * np.exp2(g.integers(-6, 6, (64, 1)))).astype(np.float32)
+    x[3] = 0.0
+    codes, scales = oracle.quantize_fp8_rows(x)
+    assert scales[3] == 1.0 and np.all(codes[3] == 0)
+    big = np.abs(x).argmax(axis=1)
+    top = codes[np.arange(64), big]
+    assert np.all((top[np.arange(64) != 3] & 0x7F) == 0x7E)
+    tq, ts = synth.quantize_fp8_rows(torch.from_numpy(x))
+    assert np.array_equal(codes, tq.view(torch.uint8).numpy())
+    assert np.array_equal(scales, ts.numpy())
