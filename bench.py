@@ -332,6 +332,23 @@ def main():
                     "hbm_GBps": ov_bytes / (ov_ms * 1e-3) / 1e9, "hbm_frac": ov_bytes / (ov_ms * 1e-3) / PEAK["hbm"]}
     del other, counts
 
+    # device fp8 quantisation of one chunk's indexer queries ([chunk, H, d] bf16 ->
+    # e4m3fn codes + per-(row, head) scales): reads 2 B and writes 1 B per element,
+    # writes 4 B per (row, head)
+    qx = torch.randn((chunk, wl.H, wl.d), device=dev).to(torch.bfloat16)
+    qc, qsc = dsa.quantize_fp8_rows(qx)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        qc, qsc = dsa.quantize_fp8_rows(qx)
+    e1.record()
+    torch.cuda.synchronize()
+    qz_ms = e0.elapsed_time(e1) / reps
+    qz_bytes = 3.0 * qx.numel() + 4.0 * qsc.numel()
+    quant_line = {"shape": [chunk, wl.H, wl.d], "us_per_launch": 1e3 * qz_ms,
+                  "hbm_GBps": qz_bytes / (qz_ms * 1e-3) / 1e9, "hbm_frac": qz_bytes / (qz_ms * 1e-3) / PEAK["hbm"]}
+    del qx, qc, qsc
+
     extra = {}
     if not args.no_all_f and "S" in roles:
         allf = "F" * len(roles)
@@ -400,6 +417,7 @@ def main():
     }
     line.update(extra)
     line["index_overlap"] = overlap_line
+    line["quantize_fp8_rows"] = quant_line
     line["decode"] = dec
     print(json.dumps(line), flush=True)
 

@@ -25,7 +25,7 @@ STATUS = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_ROLES", -3: "DSA_
 
 EXPORTS = ("dsa_indexer_topk", "dsa_indexer_topk_ws", "dsa_sparse_attn", "dsa_sparse_attn_ws",
            "indexcache_forward", "indexcache_forward_ws", "indexcache_plan", "dsa_status_string",
-           "dsa_last_error", "dsa_version", "dsa_index_overlap")
+           "dsa_last_error", "dsa_version", "dsa_index_overlap", "dsa_quantize_fp8_rows")
 
 
 class DsaError(RuntimeError):
@@ -141,6 +141,8 @@ def lib() -> ctypes.CDLL:
         L.dsa_version.restype = i32
         L.dsa_index_overlap.argtypes = [vp, vp, ctypes.c_int64, i32, vp, vp]
         L.dsa_index_overlap.restype = i32
+        L.dsa_quantize_fp8_rows.argtypes = [vp, ctypes.c_int64, i32, vp, vp, vp]
+        L.dsa_quantize_fp8_rows.restype = i32
         _lib_handle = L
     return _lib_handle
 
@@ -226,6 +228,19 @@ def sparse_attn(q: torch.Tensor, latent: torch.Tensor, idx: torch.Tensor, seqs: 
     _check(L.dsa_sparse_attn(_ptr(q), _ptr(latent), _ptr(idx), n_h, d_qk, d_v, k, float(scale), ctypes.byref(seqs),
                              _ptr(out), odt, _ptr(ws), nbytes, _stream(stream)))
     return out
+
+
+def quantize_fp8_rows(x: torch.Tensor, stream=None):
+    """dsa_quantize_fp8_rows over the last dimension of a bf16 tensor: returns
+    (codes as float8_e4m3fn of x's shape, fp32 scales of x's shape without the last dim)."""
+    if x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("a contiguous bf16 tensor is needed")
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(lib().dsa_quantize_fp8_rows(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
+    return codes.view(torch.float8_e4m3fn), scales
 
 
 def index_overlap(idx_a: torch.Tensor, idx_b: torch.Tensor, counts: Optional[torch.Tensor] = None,

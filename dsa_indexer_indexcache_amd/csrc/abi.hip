@@ -197,6 +197,17 @@ extern "C" {
 
 int dsa_version(void) { return 101; }
 
+int dsa_quantize_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, float* scales, void* stream) {
+  if (rows < 0) return fail(DSA_ERR_INVALID_ARG, "rows=%lld < 0", (long long)rows);
+  if (rows > INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "rows=%lld > 2^31 - 1", (long long)rows);
+  if (cols < 1 || cols > 65536) return fail(DSA_ERR_UNSUPPORTED, "cols=%d outside [1, 65536]", cols);
+  if (rows == 0) return DSA_OK;
+  if (!x || !codes || !scales) return fail(DSA_ERR_INVALID_ARG, "null pointer");
+  hipError_t e = dsa::launch_quantize_fp8_rows(x, rows, cols, codes, scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "fp8 quantisation launch");
+  return DSA_OK;
+}
+
 int dsa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int k, int32_t* counts,
                       void* stream) {
   if (n_rows < 0) return fail(DSA_ERR_INVALID_ARG, "n_rows=%lld < 0", (long long)n_rows);

@@ -1,5 +1,6 @@
-// Cross-layer index overlap ([IDX] §8 metrics): for every row, the number of valid
-// positions that two index tensors have in common.
+// Kernels beside the hot path: per-row fp8 quantisation of the indexer inputs
+// (device side of the fp8 setting) and the cross-layer index overlap ([IDX] §8
+// metrics): for every row, the number of valid positions two index tensors share.
 //
 // One workgroup per row.  Row B's valid positions go into an open-addressing hash
 // table in LDS (linear probing, at least twice as many slots as entries, so every
@@ -94,7 +95,77 @@ __global__ __launch_bounds__(kOvThreads) void idx_overlap_kernel(const int32_t* 
   }
 }
 
+// Per-row e4m3fn quantisation of bf16 indexer inputs.  A group of G = 2^glog lanes
+// takes one row: the row's absolute maximum (group reduction), scale = amax / 448 (1
+// for an all-zero row), y = clamp(x / scale, +-448) in fp32 (correctly rounded
+// division), and the code by the hardware OCP e4m3 conversion (round to nearest
+// even, the first operand in the low byte).  VEC: 8 elements (16 B in, 8 B out) per
+// lane access, for rows of a multiple of 8 elements on aligned buffers.
+__device__ __forceinline__ float q_clamp(float v, float scale) { return fminf(fmaxf(v / scale, -448.f), 448.f); }
+
+template <bool VEC>
+__global__ __launch_bounds__(256) void quant_fp8_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int cols,
+                                                             int glog, uint8_t* __restrict__ codes,
+                                                             float* __restrict__ scales) {
+  const int G = 1 << glog;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> glog;
+  const int lane = threadIdx.x & (G - 1);
+  if (row >= rows) return;  // whole groups leave together: the reduction stays inside a group
+  const uint16_t* xr = x + row * (int64_t)cols;
+  uint8_t* cr = codes + row * (int64_t)cols;
+  constexpr int V = VEC ? 8 : 1;
+  float amax = 0.f;
+  for (int j = lane * V; j < cols; j += G * V) {
+    if constexpr (VEC) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xr + j);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[e] << 16)), fabsf(__uint_as_float(w[e] & 0xFFFF0000u))));
+    } else {
+      amax = fmaxf(amax, fabsf(bf16_to_f32(xr[j])));
+    }
+  }
+  for (int d = G >> 1; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
+  const float scale = amax > 0.f ? amax / 448.f : 1.f;
+  for (int j = lane * V; j < cols; j += G * V) {
+    if constexpr (VEC) {
+      const uint4 v = *reinterpret_cast<const uint4*>(xr + j);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t out[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int r = __builtin_amdgcn_cvt_pk_fp8_f32(q_clamp(__uint_as_float(w[2 * h] << 16), scale),
+                                                q_clamp(__uint_as_float(w[2 * h] & 0xFFFF0000u), scale), 0, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(q_clamp(__uint_as_float(w[2 * h + 1] << 16), scale),
+                                            q_clamp(__uint_as_float(w[2 * h + 1] & 0xFFFF0000u), scale), r, true);
+        out[h] = (uint32_t)r;
+      }
+      *reinterpret_cast<uint2*>(cr + j) = make_uint2(out[0], out[1]);
+    } else {
+      cr[j] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(q_clamp(bf16_to_f32(xr[j]), scale), 0.f, 0, false) & 0xFF);
+    }
+  }
+  if (lane == 0) scales[row] = scale;
+}
+
 }  // namespace
+
+hipError_t launch_quantize_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, float* scales,
+                                    hipStream_t st) {
+  const bool vec = cols % 8 == 0 && reinterpret_cast<uintptr_t>(x) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(codes) % 8 == 0;
+  const int per_lane = vec ? 8 : 1;
+  int glog = 0;  // lanes per row: enough for one pass over the row, at most a wave
+  while (glog < 6 && ((1 << glog) * per_lane) < cols) ++glog;
+  const int64_t rows_per_block = 256 >> glog;
+  const dim3 grid((unsigned)((rows + rows_per_block - 1) / rows_per_block));
+  if (vec)
+    hipLaunchKernelGGL(quant_fp8_rows_kernel<true>, grid, dim3(256), 0, st, x, rows, cols, glog, codes, scales);
+  else
+    hipLaunchKernelGGL(quant_fp8_rows_kernel<false>, grid, dim3(256), 0, st, x, rows, cols, glog, codes, scales);
+  return hipGetLastError();
+}
 
 hipError_t launch_index_overlap(const int32_t* a, const int32_t* b, int64_t n_rows, int k, int32_t* counts,
                                 hipStream_t st) {

@@ -46,7 +46,10 @@ hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* sta
 bool indexer_fused_ok(const IndexerArgs& a);
 hipError_t launch_indexer_fused(const IndexerArgs& a, hipStream_t st);
 
-// diagnostics.hip: per-row intersection counts of two index tensors (k <= kOverlapMaxK).
+// diagnostics.hip: per-row fp8 quantisation; per-row intersection counts of two index
+// tensors (k <= kOverlapMaxK).
+hipError_t launch_quantize_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, float* scales,
+                                    hipStream_t st);
 constexpr int kOverlapMaxK = 16384;
 hipError_t launch_index_overlap(const int32_t* a, const int32_t* b, int64_t n_rows, int k, int32_t* counts,
                                 hipStream_t st);

@@ -220,6 +220,19 @@ int indexcache_plan(const char* roles, int32_t* src_layer, int32_t* n_indexer_ca
 int dsa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int k, int32_t* counts,
                       void* stream);
 
+/*
+ * Per-row fp8 quantisation of indexer inputs on the device (the fp8 setting's
+ * per-row scales, upstream of dsa_indexer_topk).  For every row r of x:
+ *   scale[r] = max_j |x[r, j]| / 448 (1 for an all-zero row), computed in fp32;
+ *   codes[r, j] = e4m3fn(clamp(x[r, j] / scale[r], -448, 448)), fp32 division, round
+ *                 to nearest even, sign kept (OCP e4m3fn, max 448).
+ *   x [rows, cols] bf16 (device); codes [rows, cols] e4m3fn bytes, scales [rows] fp32
+ *   (device, written).  A q_idx [n_q, H, d] tensor is rows = n_q * H, cols = d.
+ * 1 <= cols <= 65536 and rows < 2^31 (else DSA_ERR_UNSUPPORTED); rows == 0 is a no-op;
+ * rows < 0 or a null pointer gives DSA_ERR_INVALID_ARG.
+ */
+int dsa_quantize_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, float* scales, void* stream);
+
 /* ---------------------------------------------------------------- misc */
 const char* dsa_status_string(int status); /* static string                         */
 const char* dsa_last_error(void);          /* thread-local detail of the last error */

@@ -160,3 +160,12 @@ def test_index_overlap_validation():
     assert L.dsa_index_overlap(None, None, 4, 16385, None, None) == -4        # k too large
     assert L.dsa_index_overlap(None, None, -1, 16, None, None) == -1          # negative row count
     assert L.dsa_index_overlap(None, None, 4, 16, None, None) == -1           # null pointers
+
+
+def test_quantize_fp8_rows_validation():
+    L = dsa.lib()
+    assert L.dsa_quantize_fp8_rows(None, 0, 128, None, None, None) == 0      # no rows: a no-op
+    assert L.dsa_quantize_fp8_rows(None, 4, 0, None, None, None) == -4       # cols < 1
+    assert L.dsa_quantize_fp8_rows(None, 4, 65537, None, None, None) == -4   # cols too large
+    assert L.dsa_quantize_fp8_rows(None, 4, 128, None, None, None) == -1     # null pointers
+    assert L.dsa_quantize_fp8_rows(None, 2 ** 31, 128, None, None, None) == -4  # too many rows

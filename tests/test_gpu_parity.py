@@ -357,3 +357,55 @@ def test_index_overlap_between_two_f_layers():
     want = np.array([round(oracle.overlap(a[i], b[i], k) * k) for i in range(L)], dtype=np.int32)
     assert np.array_equal(got.cpu().numpy(), want)
     assert got[:k].eq(torch.arange(1, k + 1, device=DEV, dtype=torch.int32)).all()   # t < k: all rows visible
+
+
+# --------------------------------------------------------------------------- device fp8 quantisation
+
+def _quant_rows(rows, cols, seed):
+    """bf16 rows of mixed magnitude; row 0 is all zero, row 1 holds exact e4m3 ties at
+    scale 1 (normal and subnormal midpoints, both signs, a negative that rounds to zero),
+    row 2 is tiny (codes in the subnormal range), row 3 has a single non-zero entry."""
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((rows, cols)).astype(np.float32) * (2.0 ** g.integers(-12, 12, (rows, 1)))
+    x[0] = 0.0
+    ties = np.array([448.0, 1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, -(2.0 ** -10), 0.0, -0.0,
+                     240.0 + 8.0, 13.0, -416.0 - 16.0], dtype=np.float32)
+    x[1] = np.resize(ties, cols)
+    x[1, 0] = 448.0
+    x[2] *= 2.0 ** -20
+    x[3] = 0.0
+    x[3, cols // 2] = -3.5
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    return xb, xb.to(torch.float32).numpy()
+
+
+@pytest.mark.parametrize("rows,cols", [(1001, 128), (37, 100), (9, 577), (4, 1)])
+def test_quantize_fp8_rows_bit_exact(rows, cols):
+    announce("fp8 quantisation rows=%d cols=%d" % (rows, cols))
+    xb, xf = _quant_rows(rows, cols, seed=rows + cols)
+    codes, scales = dsa.quantize_fp8_rows(xb.to(DEV))
+    torch.cuda.synchronize()
+    want_codes, want_scales = oracle.quantize_fp8_rows(xf)
+    np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), want_scales.view(np.uint32))
+    np.testing.assert_array_equal(codes.view(torch.uint8).cpu().numpy(), want_codes)
+
+
+def test_quantize_fp8_rows_feeds_the_indexer():
+    """The fp8 indexer path end to end from bf16 inputs: q_idx / k_idx quantised on the
+    device (codes and scales equal to the oracle's quantisation of the same bf16
+    values), then indexer + top-k checked against the oracle on those inputs."""
+    announce("fp8 quantisation -> indexer")
+    L, H, d, k = 1500, 16, 128, 256
+    li = layer(L, H, d, 16)
+    seqs = dsa.Seqs.prefill(L)
+    qc, qs = dsa.quantize_fp8_rows(li.q_idx.contiguous())
+    kc, ks = dsa.quantize_fp8_rows(li.k_idx.contiguous())
+    torch.cuda.synchronize()
+    for codes, scales, src in ((qc, qs, li.q_idx), (kc, ks, li.k_idx)):
+        want_c, want_s = oracle.quantize_fp8_rows(src.float().cpu().numpy())
+        np.testing.assert_array_equal(codes.view(torch.uint8).cpu().numpy(), want_c)
+        np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), want_s.view(np.uint32))
+    idx, sc = dsa.indexer_topk(qc, kc, li.w, k, seqs, q_scale=qs, k_scale=ks, want_scores=True)
+    torch.cuda.synchronize()
+    q8 = synth.LayerInputs(qc, qs, kc, ks, li.w, li.q, li.latent)
+    check_indexer(OracleView(q8), seqs, sample_rows(L, k, 200, seed=11), k, idx, sc, exact=False)
