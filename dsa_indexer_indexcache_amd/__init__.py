@@ -230,15 +230,23 @@ def sparse_attn(q: torch.Tensor, latent: torch.Tensor, idx: torch.Tensor, seqs: 
     return out
 
 
-def quantize_fp8_rows(x: torch.Tensor, stream=None):
+def quantize_fp8_rows(x: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                      scales: Optional[torch.Tensor] = None, stream=None):
     """dsa_quantize_fp8_rows over the last dimension of a bf16 tensor: returns
-    (codes as float8_e4m3fn of x's shape, fp32 scales of x's shape without the last dim)."""
+    (codes as float8_e4m3fn of x's shape, fp32 scales of x's shape without the last dim);
+    codes (uint8 or float8_e4m3fn) and scales may be passed in preallocated."""
     if x.dtype != torch.bfloat16 or not x.is_contiguous():
         raise ValueError("a contiguous bf16 tensor is needed")
     cols = x.shape[-1]
     rows = x.numel() // cols if cols else 0
-    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    if codes.shape != x.shape or codes.element_size() != 1 or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous 1-byte tensor of x's shape")
+    if scales.shape != x.shape[:-1] or scales.dtype != torch.float32 or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous fp32 tensor of x's shape without the last dim")
     _check(lib().dsa_quantize_fp8_rows(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes.view(torch.float8_e4m3fn), scales
 

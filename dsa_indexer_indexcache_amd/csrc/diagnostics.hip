@@ -114,10 +114,14 @@ __global__ __launch_bounds__(256) void quant_fp8_rows_kernel(const uint16_t* __r
   const uint16_t* xr = x + row * (int64_t)cols;
   uint8_t* cr = codes + row * (int64_t)cols;
   constexpr int V = VEC ? 8 : 1;
+  // VEC: the lane's first 16 B stay in registers for the second pass, so a row of at
+  // most 8 G elements (one access per lane) is read from memory once
+  uint4 first = make_uint4(0, 0, 0, 0);
   float amax = 0.f;
   for (int j = lane * V; j < cols; j += G * V) {
     if constexpr (VEC) {
       const uint4 v = *reinterpret_cast<const uint4*>(xr + j);
+      if (j == lane * V) first = v;
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(256) void quant_fp8_rows_kernel(const uint16_t* __r
   const float scale = amax > 0.f ? amax / 448.f : 1.f;
   for (int j = lane * V; j < cols; j += G * V) {
     if constexpr (VEC) {
-      const uint4 v = *reinterpret_cast<const uint4*>(xr + j);
+      const uint4 v = j == lane * V ? first : *reinterpret_cast<const uint4*>(xr + j);
       const uint32_t w[4] = {v.x, v.y, v.z, v.w};
       uint32_t out[2];
 #pragma unroll
