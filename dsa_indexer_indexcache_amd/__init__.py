@@ -160,6 +160,50 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return t.data_ptr()
 
 
+def _req(t: Optional[torch.Tensor], name: str, dtypes, shape=None, optional: bool = False):
+    """Checks one tensor argument before it is handed to the library as a raw pointer:
+    dtype (one of `dtypes`), exact shape (None entries are free) and contiguity.  Where
+    the tensors live is checked afterwards, for all of them together (`_on_gpu`).
+    Returns the tensor; raises ValueError."""
+    if t is None:
+        if optional:
+            return None
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch tensor" % name)
+    if t.dtype not in dtypes:
+        raise ValueError("%s must be %s, got %s" % (name, " or ".join(str(d) for d in dtypes), t.dtype))
+    if shape is not None:
+        if t.dim() != len(shape) or any(want is not None and int(got) != int(want)
+                                        for got, want in zip(t.shape, shape)):
+            raise ValueError("%s must have shape %s, got %s" % (
+                name, tuple("*" if x is None else x for x in shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _on_gpu(**tensors):
+    """Every given tensor (None entries skipped) lives on one and the same GPU."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("%s must be on a GPU, got %s" % (name, t.device))
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, the other tensors on %s" % (name, t.device, dev))
+
+
+_BF16 = (torch.bfloat16,)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+_QK = (torch.bfloat16, torch.float8_e4m3fn)
+_OUT = (torch.float32, torch.bfloat16)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return DSA_BF16
@@ -192,15 +236,30 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, k: i
                  want_scores: bool = False, idx_out: Optional[torch.Tensor] = None,
                  score_out: Optional[torch.Tensor] = None, stream=None):
     """dsa_indexer_topk: returns (idx int32 [n_q, k], scores fp32 [n_q, k] or None)."""
+    _req(q_idx, "q_idx", _QK, (None, None, None))
     n_q, H, d = q_idx.shape
+    dev = q_idx.device
+    _req(k_idx, "k_idx", (q_idx.dtype,), (None, d))
+    _req(w, "w", _BF16, (n_q, H))
+    fp8 = q_idx.dtype == torch.float8_e4m3fn
+    _req(q_scale, "q_scale", _F32, (n_q, H), optional=not fp8)
+    _req(k_scale, "k_scale", _F32, (k_idx.shape[0],), optional=not fp8)
+    if not fp8 and (q_scale is not None or k_scale is not None):
+        raise ValueError("the bf16 indexer takes no scales")
     if seqs is None:
         seqs = Seqs.prefill(n_q, k_idx.shape[0], q_pos0=k_idx.shape[0] - n_q)
+    if seqs.n_q != n_q or seqs.n_k > k_idx.shape[0]:
+        raise ValueError("seqs describes %d queries over %d keys; tensors hold %d and %d"
+                         % (seqs.n_q, seqs.n_k, n_q, k_idx.shape[0]))
     dt = _dtype_code(q_idx)
-    dev = q_idx.device
     if idx_out is None:
         idx_out = torch.empty((n_q, k), dtype=torch.int32, device=dev)
+    _req(idx_out, "idx_out", _I32, (n_q, k))
     if want_scores and score_out is None:
         score_out = torch.empty((n_q, k), dtype=torch.float32, device=dev)
+    _req(score_out, "score_out", _F32, (n_q, k), optional=True)
+    _on_gpu(q_idx=q_idx, k_idx=k_idx, w=w, q_scale=q_scale, k_scale=k_scale, idx_out=idx_out,
+            score_out=score_out)
     L = lib()
     nbytes = L.dsa_indexer_topk_ws(dt, H, d, k, ctypes.byref(seqs))
     ws = _workspace(nbytes, dev)
@@ -213,15 +272,24 @@ def sparse_attn(q: torch.Tensor, latent: torch.Tensor, idx: torch.Tensor, seqs: 
                 scale: Optional[float] = None, d_v: int = 512, out_dtype=torch.float32,
                 out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """dsa_sparse_attn: out [n_q, n_h, d_v] (fp32 by default)."""
+    _req(q, "q", _BF16, (None, None, None))
     n_q, n_h, d_qk = q.shape
+    dev = q.device
+    _req(latent, "latent", _BF16, (None, d_qk))
+    _req(idx, "idx", _I32, (n_q, None))
     k = idx.shape[1]
     if seqs is None:
         seqs = Seqs.prefill(n_q, latent.shape[0], q_pos0=latent.shape[0] - n_q)
+    if seqs.n_q != n_q or seqs.n_k > latent.shape[0]:
+        raise ValueError("seqs describes %d queries over %d keys; tensors hold %d and %d"
+                         % (seqs.n_q, seqs.n_k, n_q, latent.shape[0]))
     if scale is None:
         scale = d_qk ** -0.5
-    odt = DSA_FP32 if out_dtype == torch.float32 else DSA_BF16
     if out is None:
         out = torch.empty((n_q, n_h, d_v), dtype=out_dtype, device=q.device)
+    _req(out, "out", _OUT, (n_q, n_h, d_v))
+    odt = DSA_FP32 if out.dtype == torch.float32 else DSA_BF16
+    _on_gpu(q=q, latent=latent, idx=idx, out=out)
     L = lib()
     nbytes = L.dsa_sparse_attn_ws(n_h, d_qk, d_v, k, ctypes.byref(seqs))
     ws = _workspace(nbytes, q.device)
@@ -235,18 +303,18 @@ def quantize_fp8_rows(x: torch.Tensor, codes: Optional[torch.Tensor] = None,
     """dsa_quantize_fp8_rows over the last dimension of a bf16 tensor: returns
     (codes as float8_e4m3fn of x's shape, fp32 scales of x's shape without the last dim);
     codes (uint8 or float8_e4m3fn) and scales may be passed in preallocated."""
-    if x.dtype != torch.bfloat16 or not x.is_contiguous():
-        raise ValueError("a contiguous bf16 tensor is needed")
+    if not isinstance(x, torch.Tensor) or x.dim() < 1:
+        raise ValueError("x must be a bf16 tensor with at least one dimension")
+    _req(x, "x", _BF16, tuple(x.shape))
     cols = x.shape[-1]
     rows = x.numel() // cols if cols else 0
     if codes is None:
         codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     if scales is None:
         scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    if codes.shape != x.shape or codes.element_size() != 1 or not codes.is_contiguous():
-        raise ValueError("codes must be a contiguous 1-byte tensor of x's shape")
-    if scales.shape != x.shape[:-1] or scales.dtype != torch.float32 or not scales.is_contiguous():
-        raise ValueError("scales must be a contiguous fp32 tensor of x's shape without the last dim")
+    _req(codes, "codes", (torch.uint8, torch.float8_e4m3fn), tuple(x.shape))
+    _req(scales, "scales", _F32, tuple(x.shape[:-1]))
+    _on_gpu(x=x, codes=codes, scales=scales)
     _check(lib().dsa_quantize_fp8_rows(_ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
     return codes.view(torch.float8_e4m3fn), scales
 
@@ -255,11 +323,13 @@ def index_overlap(idx_a: torch.Tensor, idx_b: torch.Tensor, counts: Optional[tor
                   stream=None) -> torch.Tensor:
     """dsa_index_overlap: counts[i] = |valid(idx_a[i]) ∩ valid(idx_b[i])| (int32); divide by k
     for the overlap fraction."""
-    if idx_a.shape != idx_b.shape or idx_a.dim() != 2:
-        raise ValueError("two [n_rows, k] index tensors of one shape are needed")
+    _req(idx_a, "idx_a", _I32, (None, None))
     n_rows, k = idx_a.shape
+    _req(idx_b, "idx_b", _I32, (n_rows, k))
     if counts is None:
         counts = torch.empty((n_rows,), dtype=torch.int32, device=idx_a.device)
+    _req(counts, "counts", _I32, (n_rows,))
+    _on_gpu(idx_a=idx_a, idx_b=idx_b, counts=counts)
     _check(lib().dsa_index_overlap(_ptr(idx_a), _ptr(idx_b), n_rows, k, _ptr(counts), _stream(stream)))
     return counts
 
@@ -289,10 +359,23 @@ def indexcache_forward(roles: str, layers: Sequence[dict], k: int, seqs: Optiona
     if len(layers) != n_layers:
         raise ValueError("one layer dict per role")
     l0 = layers[0]
+    _req(l0.get("q"), "layers[0].q", _BF16, (None, None, None))
     n_q, n_h, d_qk = l0["q"].shape
     dev = l0["q"].device
     f0 = next(i for i, r in enumerate(roles) if r == "F") if "F" in roles else 0
     qi = layers[f0].get("q_idx")
+    n_k = l0["latent"].shape[0] if l0.get("latent") is not None else 0
+    for l, d in enumerate(layers):
+        _req(d.get("q"), "layers[%d].q" % l, _BF16, (n_q, n_h, d_qk))
+        _req(d.get("latent"), "layers[%d].latent" % l, _BF16, (n_k, d_qk))
+        if roles[l:l + 1] == "F":
+            _req(d.get("q_idx"), "layers[%d].q_idx" % l, _QK, (n_q, None, None))
+            H_, d_ = d["q_idx"].shape[1:]
+            _req(d.get("k_idx"), "layers[%d].k_idx" % l, (d["q_idx"].dtype,), (n_k, d_))
+            _req(d.get("w"), "layers[%d].w" % l, _BF16, (n_q, H_))
+            fp8 = d["q_idx"].dtype == torch.float8_e4m3fn
+            _req(d.get("q_scale"), "layers[%d].q_scale" % l, _F32, (n_q, H_), optional=not fp8)
+            _req(d.get("k_scale"), "layers[%d].k_scale" % l, _F32, (n_k,), optional=not fp8)
     if seqs is None:
         seqs = Seqs.prefill(n_q, l0["latent"].shape[0], q_pos0=l0["latent"].shape[0] - n_q)
     shape = Shape()
@@ -306,9 +389,20 @@ def indexcache_forward(roles: str, layers: Sequence[dict], k: int, seqs: Optiona
     shape.out_rows = int(out_rows or max(n_q, 1))
     if outs is None:
         outs = [torch.empty((shape.out_rows, n_h, d_v), dtype=out_dtype, device=dev) for _ in range(n_layers)]
+    if len(outs) != n_layers:
+        raise ValueError("one output tensor per layer")
+    for l, o in enumerate(outs):
+        _req(o, "outs[%d]" % l, (out_dtype,), (shape.out_rows, n_h, d_v))
     if index_cache is None:
         index_cache = torch.empty((shape.index_rows, k), dtype=torch.int32, device=dev)
+    _req(index_cache, "index_cache", _I32, (shape.index_rows, k))
     score_cache = torch.empty((shape.index_rows, k), dtype=torch.float32, device=dev) if want_scores else None
+    if ws is not None:
+        _req(ws, "ws", (torch.uint8,), (None,))
+    named = {"outs[%d]" % l: o for l, o in enumerate(outs)}
+    for l, d in enumerate(layers):
+        named.update({"layers[%d].%s" % (l, n): t for n, t in d.items() if isinstance(t, torch.Tensor)})
+    _on_gpu(index_cache=index_cache, ws=ws, **named)
     arr = (Layer * n_layers)()
     for l, d in enumerate(layers):
         for name in ("q_idx", "q_scale", "k_idx", "k_scale", "w", "q", "latent"):

@@ -212,6 +212,7 @@ int dsa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows
                       void* stream) {
   if (n_rows < 0) return fail(DSA_ERR_INVALID_ARG, "n_rows=%lld < 0", (long long)n_rows);
   if (k < 1 || k > dsa::kOverlapMaxK) return fail(DSA_ERR_UNSUPPORTED, "k=%d outside [1, %d]", k, dsa::kOverlapMaxK);
+  if (n_rows > INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "n_rows=%lld > 2^31 - 1", (long long)n_rows);
   if (n_rows == 0) return DSA_OK;
   if (!idx_a || !idx_b || !counts) return fail(DSA_ERR_INVALID_ARG, "null pointer");
   hipError_t e = dsa::launch_index_overlap(idx_a, idx_b, n_rows, k, counts, (hipStream_t)stream);

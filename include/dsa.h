@@ -215,7 +215,8 @@ int indexcache_plan(const char* roles, int32_t* src_layer, int32_t* n_indexer_ca
  * (row order does not matter; valid entries of a row must be distinct, as the
  * indexer writes them).  Overlap^(l,l') of the row = counts[i] / k.
  *   idx_a, idx_b [n_rows, k] int32 (device);  counts [n_rows] int32 (device, written)
- * 1 <= k <= 16384; n_rows == 0 is a no-op.  Exact (integer) result.
+ * 1 <= k <= 16384 and n_rows < 2^31 (else DSA_ERR_UNSUPPORTED); n_rows == 0 is a
+ * no-op; n_rows < 0 or a null pointer gives DSA_ERR_INVALID_ARG.  Exact (integer) result.
  */
 int dsa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows, int k, int32_t* counts,
                       void* stream);

@@ -160,6 +160,7 @@ def test_index_overlap_validation():
     assert L.dsa_index_overlap(None, None, 4, 16385, None, None) == -4        # k too large
     assert L.dsa_index_overlap(None, None, -1, 16, None, None) == -1          # negative row count
     assert L.dsa_index_overlap(None, None, 4, 16, None, None) == -1           # null pointers
+    assert L.dsa_index_overlap(None, None, 2 ** 31, 16, None, None) == -4     # rows beyond int32
 
 
 def test_quantize_fp8_rows_validation():
@@ -169,3 +170,34 @@ def test_quantize_fp8_rows_validation():
     assert L.dsa_quantize_fp8_rows(None, 4, 65537, None, None, None) == -4   # cols too large
     assert L.dsa_quantize_fp8_rows(None, 4, 128, None, None, None) == -1     # null pointers
     assert L.dsa_quantize_fp8_rows(None, 2 ** 31, 128, None, None, None) == -4  # too many rows
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    """The Python binding checks dtype, shape, contiguity and device of every tensor it
+    turns into a raw pointer (an int64 index tensor, as torch.topk returns, would otherwise
+    be read as int32; a short counts tensor would be written out of bounds)."""
+    import torch
+    cpu32 = torch.zeros((4, 16), dtype=torch.int32)
+    with pytest.raises(ValueError, match="int32"):
+        dsa.index_overlap(cpu32.to(torch.int64), cpu32)
+    with pytest.raises(ValueError, match="GPU"):
+        dsa.index_overlap(cpu32, cpu32)
+    with pytest.raises(ValueError, match="shape"):
+        dsa.index_overlap(torch.zeros((4, 16, 1), dtype=torch.int32), cpu32)
+    with pytest.raises(ValueError, match="int32"):
+        dsa.sparse_attn(torch.zeros((4, 16, 576), dtype=torch.bfloat16),
+                        torch.zeros((8, 576), dtype=torch.bfloat16), cpu32.to(torch.int64))
+    with pytest.raises(ValueError, match="GPU"):
+        dsa.sparse_attn(torch.zeros((4, 16, 576), dtype=torch.bfloat16),
+                        torch.zeros((8, 576), dtype=torch.bfloat16), cpu32)
+    with pytest.raises(ValueError, match="contiguous"):
+        dsa.sparse_attn(torch.zeros((16, 4, 576), dtype=torch.bfloat16).transpose(0, 1),
+                        torch.zeros((8, 576), dtype=torch.bfloat16), cpu32)
+    q = torch.zeros((4, 8, 64), dtype=torch.bfloat16)
+    kk = torch.zeros((4, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="w must"):
+        dsa.indexer_topk(q, kk, torch.zeros((4, 8), dtype=torch.float32), 2)
+    with pytest.raises(ValueError, match="k_idx must"):
+        dsa.indexer_topk(q, kk.to(torch.float32), torch.zeros((4, 8), dtype=torch.bfloat16), 2)
+    with pytest.raises(ValueError, match="x must"):
+        dsa.quantize_fp8_rows(torch.zeros((4, 8), dtype=torch.float32))

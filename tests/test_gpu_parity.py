@@ -379,11 +379,28 @@ def _quant_rows(rows, cols, seed):
     return xb, xb.to(torch.float32).numpy()
 
 
-@pytest.mark.parametrize("rows,cols", [(1001, 128), (37, 100), (9, 577), (4, 1)])
+@pytest.mark.parametrize("rows,cols", [(1001, 128), (37, 100), (9, 577), (4, 1), (33, 1024), (17, 24), (9, 40)])
 def test_quantize_fp8_rows_bit_exact(rows, cols):
     announce("fp8 quantisation rows=%d cols=%d" % (rows, cols))
     xb, xf = _quant_rows(rows, cols, seed=rows + cols)
     codes, scales = dsa.quantize_fp8_rows(xb.to(DEV))
+    torch.cuda.synchronize()
+    want_codes, want_scales = oracle.quantize_fp8_rows(xf)
+    np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), want_scales.view(np.uint32))
+    np.testing.assert_array_equal(codes.view(torch.uint8).cpu().numpy(), want_codes)
+
+
+def test_quantize_fp8_rows_misaligned_view():
+    """A bf16 view one element past an aligned base (rows of a multiple of 8 elements):
+    the 16-byte vector path does not apply, the per-element path must give the same codes."""
+    announce("fp8 quantisation misaligned view")
+    rows, cols = 21, 128
+    xb, xf = _quant_rows(rows, cols, seed=77)
+    buf = torch.empty(rows * cols + 1, dtype=torch.bfloat16, device=DEV)
+    buf[1:] = xb.reshape(-1).to(DEV)
+    x = buf[1:].view(rows, cols)
+    assert x.data_ptr() % 16 != 0
+    codes, scales = dsa.quantize_fp8_rows(x)
     torch.cuda.synchronize()
     want_codes, want_scales = oracle.quantize_fp8_rows(xf)
     np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), want_scales.view(np.uint32))

@@ -124,6 +124,30 @@ def test_hand_indexcache_plan():
             indexcache_plan(bad)
 
 
+# ----------------------------------------------------------------------------- acceptance tolerance
+
+def test_tolerance_row_hand_values():
+    """The float acceptance threshold is 1e-3 times the largest |I[t, s]| over the visible
+    prefix (the score tolerance the parity rules state).  Hand rows separate it from the
+    plausible wrong forms: max(I) instead of max|I| (all-negative row), sum|I| or the
+    mean (mixed row), and a relative factor other than 1e-3 (single element)."""
+    assert oracle.tolerance_row(np.array([-3.0, -1.0, -2.0])) == pytest.approx(3e-3, rel=0, abs=1e-18)
+    assert oracle.tolerance_row(np.array([2.0, -5.0, 1.0])) == pytest.approx(5e-3, rel=0, abs=1e-18)
+    assert oracle.tolerance_row(np.array([7.0])) == pytest.approx(7e-3, rel=0, abs=1e-18)
+    assert oracle.tolerance_row(np.array([0.0, -0.0])) == 0.0
+    assert oracle.tolerance_row(np.array([])) == 0.0
+    assert oracle.tolerance_row(np.array([2.0, -5.0, 1.0]), rel=0.5) == 2.5
+
+
+def test_parity_rules_use_the_stated_thresholds():
+    """The thresholds every float parity test applies: scores within 1e-3 x row max |I|,
+    mean recall >= 0.999, attention max abs error <= 1e-2."""
+    import parity
+    assert parity.SCORE_REL == 1e-3
+    assert parity.RECALL_MIN == 0.999
+    assert parity.ATTN_ATOL == 1e-2
+
+
 # ----------------------------------------------------------------------------- exactness (C6)
 
 def test_integer_indexer_is_exact_in_fp64():
