@@ -13,7 +13,13 @@ definitions on the source pages.  Citations use two page titles:
         error decomposition §3, DeepSeek-V3.2 lightning indexer §4, GLM-5 index
         mask and deterministic top-k §6.4-§6.5, index-quality metrics §8)
   [IC]  "读懂 IndexCache：从 DSA 的选词开销到跨层索引复用"
-        (F/S layer roles §1.1, the cache update loop and the {2,5,8} example §1.2)
+        (F/S layer roles §1.1, the cache update loop and the {2,5,8} example §1.2,
+        the multi-layer distillation loss §3.1)
+
+Modules: formats (storage formats), dsa (indexer, top-k, attention, IndexCache loop,
+index-quality metrics, the sparse-training indexer loss), upstream (the indexer's
+projections, key LayerNorm, rotary encoding, cache append; [IDX] §6.4, §4), csa (the
+compressed-block selection of [IDX] §5).
 
 Every function here is pinned by tests under tests/ against closed forms,
 hand-derived fixtures, brute force and library routines (see test_oracle_*.py).
@@ -21,8 +27,11 @@ hand-derived fixtures, brute force and library routines (see test_oracle_*.py).
 from .formats import decode_bf16, decode_e4m3fn, e4m3fn_table, dequant_rows, encode_e4m3fn, quantize_fp8_rows
 from .dsa import (indexer_row, indexer_row_int2, topk_row, attn_row, dense_attn_row,
                   indexcache_plan, indexcache_forward, RoleError, tolerance_row,
-                  captured_mass, overlap)
+                  captured_mass, overlap, head_mean_distribution, captured_mass_at_k, recall_at_k,
+                  sparse_attention_weights, indexer_kl_row, multilayer_kl)
 
 __all__ = ["decode_bf16", "decode_e4m3fn", "e4m3fn_table", "dequant_rows", "encode_e4m3fn", "quantize_fp8_rows", "indexer_row",
            "indexer_row_int2", "topk_row", "attn_row", "dense_attn_row", "indexcache_plan",
-           "indexcache_forward", "RoleError", "tolerance_row", "captured_mass", "overlap"]
+           "indexcache_forward", "RoleError", "tolerance_row", "captured_mass", "overlap",
+           "head_mean_distribution", "captured_mass_at_k", "recall_at_k", "sparse_attention_weights",
+           "indexer_kl_row", "multilayer_kl"]

@@ -120,6 +120,87 @@ def captured_mass(alpha_row: np.ndarray, idx: np.ndarray) -> float:
     return float(alpha_row[sel].sum())
 
 
+def head_mean_distribution(alpha: np.ndarray) -> np.ndarray:
+    """The attention distribution of one query aggregated over heads: the per-head
+    distributions alpha [n_h, n] summed over heads, then L1-normalised over positions
+    ([IDX] §4.1, the dense warm-up target p_t).  Each row of alpha sums to 1, so this is
+    the mean over heads."""
+    p = alpha.sum(axis=0)
+    return p / p.sum()
+
+
+def captured_mass_at_k(alpha: np.ndarray, idx: np.ndarray):
+    """CapturedMass@k of one query ([IDX] §8 item 1): sum over s in S_t of the dense
+    attention weight alpha^dense[t, s], per head (alpha [n_h, t+1]) and for the
+    head-aggregated distribution p_t.  Returns (per_head [n_h], aggregated); the missed
+    mass is 1 minus either."""
+    sel = np.asarray(idx)
+    sel = sel[sel >= 0]
+    per_head = alpha[:, sel].sum(axis=1)
+    return per_head, float(head_mean_distribution(alpha)[sel].sum())
+
+
+def recall_at_k(alpha: np.ndarray, idx_model: np.ndarray, k: int):
+    """Recall@k of one query ([IDX] §8 item 2): the oracle selection S^oracle = the k
+    positions of largest head-aggregated dense weight p_t (same total order as the
+    indexer's top-k: weight descending, position ascending), against the model's
+    selection S^model (valid entries of idx_model).  Returns
+    (|S^oracle ∩ S^model| / |S^oracle|, S^oracle row as topk_row returns it)."""
+    p = head_mean_distribution(alpha)
+    row, _, m = topk_row(p, k)
+    oracle_set = set(int(x) for x in row[:m])
+    model_set = set(int(x) for x in np.asarray(idx_model) if x >= 0)
+    return len(oracle_set & model_set) / float(m), row
+
+
+# ---------------------------------------------------------------------------
+# sparse-training indexer loss  ([IDX] §4.2 KL over S_t; [IC] §3.1 multi-layer form)
+# ---------------------------------------------------------------------------
+
+def sparse_attention_weights(q_t: np.ndarray, latent: np.ndarray, idx: np.ndarray, scale: float):
+    """The main attention's weights over the selected set: per head, softmax over
+    s in S_t of scale * q[h] . c[s] ([IDX] §2).  Returns (alpha_hat [n_h, |S|], sel)."""
+    sel = np.asarray(idx)
+    sel = sel[sel >= 0]
+    z = scale * (q_t @ latent[sel].T)
+    z -= z.max(axis=1, keepdims=True)
+    a = np.exp(z)
+    return a / a.sum(axis=1, keepdims=True), sel
+
+
+def indexer_kl_row(q_t: np.ndarray, latent: np.ndarray, idx: np.ndarray, scores: np.ndarray, scale: float) -> float:
+    """D_KL(p_{t,S_t} || Softmax(I_{t,S_t})) of one query ([IDX] §4.2).
+
+    p_{t,S_t}: the main attention's weights over S_t (sparse attention, softmax over S_t
+    per head), summed over heads and L1-normalised; Softmax(I_{t,S_t}): the indexer
+    scores of the same positions, softmax over S_t.  `scores[j]` is the indexer score of
+    position idx[j] (slots with idx < 0 ignored).  Terms with p = 0 contribute 0."""
+    ii = np.asarray(idx)
+    ok = ii >= 0
+    alpha, _ = sparse_attention_weights(q_t, latent, ii, scale)
+    p = head_mean_distribution(alpha)
+    I = np.asarray(scores, dtype=np.float64)[ok]
+    logpi = I - I.max()
+    logpi = logpi - np.log(np.exp(logpi).sum())
+    nz = p > 0
+    return float(np.sum(p[nz] * (np.log(p[nz]) - logpi[nz])))
+
+
+def multilayer_kl(layers, idx: np.ndarray, scores: np.ndarray, scale: float) -> float:
+    """The multi-layer distillation loss of one F layer that serves m S layers
+    ([IC] §3.1): (1/(m+1)) sum_{j=0..m} sum_t D_KL(p_t^{(l+j)} || q_t^{(l)}), where
+    q_t^{(l)} = Softmax(I_{t,S_t}) is the F layer's indexer distribution and p^{(l+j)}
+    the attention distribution of layer l+j over the same S_t.
+
+    layers: m+1 dicts with 'q' [n, n_h, D] (the checked rows) and 'latent' [n_k, D];
+    idx, scores [n, k] (the F layer's selection and indexer scores)."""
+    tot = 0.0
+    for L in layers:
+        for i in range(idx.shape[0]):
+            tot += indexer_kl_row(L["q"][i], L["latent"], idx[i], scores[i], scale)
+    return tot / len(layers)
+
+
 def overlap(idx_a: np.ndarray, idx_b: np.ndarray, k: int) -> float:
     """|S^(l) intersect S^(l+1)| / k for one query row."""
     a = set(int(x) for x in idx_a if x >= 0)
