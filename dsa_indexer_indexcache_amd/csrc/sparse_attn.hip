@@ -259,10 +259,11 @@ constexpr int kMaxWaves = 8;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef v4i16 __attribute__((address_space(3))) lds_v4i16;
 
+template <int HG, int NW>
 struct PairSmem {
   uint8_t tile[kNBuf][kTileBytes];
-  f32x4 xs[kMaxWaves][4][64];   // partial score exchange, [wave][register quad][lane]
-  int idx[kIdxMax];             // the row's selected positions (-1 = skip)
+  f32x4 xs[NW][2 * HG][64];     // partial score exchange, [wave][register quad][lane]
+  int idx[kIdxMax];             // the split's selected positions (-1 = skip)
   float bias[kIdxMax];          // 0 for a usable slot, -inf for a skipped one
 };
 
@@ -293,35 +294,45 @@ __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
   return (uint32_t)((chunk >> 3) * (kBlk * 128) + row * 128 + 16 * ((chunk & 7) ^ (row & 7)));
 }
 
+// Workgroup b of the grid takes query row b % n_q, head group (b / n_q) % hgroups and
+// split b / (n_q hgroups) of the row's index list: consecutive workgroups take
+// consecutive rows, so with n_q = 8 every workgroup of a row is dispatched to the
+// same XCD (workgroups go round-robin over the 8 XCDs) and the head groups of a row
+// re-read its gathered latent rows from that XCD's L2.
 template <int HG, int NW>
-__global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* __restrict__ q,
-                                                               const uint16_t* __restrict__ latent,
-                                                               const int32_t* __restrict__ idx, int n_h, int k,
-                                                               float scale_log2, dsa_seqs seqs, int64_t n_q, int splits,
-                                                               float* __restrict__ out_f32,
-                                                               uint16_t* __restrict__ out_bf16,
-                                                               float* __restrict__ part_o, float* __restrict__ part_ml) {
-  __shared__ PairSmem sm;
+__global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_t* __restrict__ q,
+                                                                   const uint16_t* __restrict__ latent,
+                                                                   const int32_t* __restrict__ idx, int n_h, int k,
+                                                                   float scale_log2, dsa_seqs seqs, int64_t n_q,
+                                                                   int hgroups, int splits,
+                                                                   float* __restrict__ out_f32,
+                                                                   uint16_t* __restrict__ out_bf16,
+                                                                   float* __restrict__ part_o,
+                                                                   float* __restrict__ part_ml) {
+  __shared__ PairSmem<HG, NW> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int nwaves = NW;
   const int pair = wave >> 1, vh = wave & 1;
-  const int64_t i = blockIdx.x / splits;
-  const int split = blockIdx.x % splits;
-  if (i >= n_q) return;
+  const uint32_t nq32 = (uint32_t)n_q;  // the grid is n_q * hgroups * splits < 2^32 workgroups
+  const int64_t i = blockIdx.x % nq32;
+  const uint32_t rest = blockIdx.x / nq32;
+  const int hgi = (int)(rest % (uint32_t)hgroups);
+  const int split = (int)(rest / (uint32_t)hgroups);
+  if (split >= splits) return;
   const int b = seq_of_row(seqs, i);
   const int64_t p = seqs.q_pos0[b] + (i - seqs.q_start[b]);
   const uint16_t* lat = latent + seqs.k_start[b] * kDqk;
   const int c = lane & 15, g = lane >> 4;
-  const int head0 = 16 * HG * pair;
+  const int head0 = 8 * HG * NW * hgi + 16 * HG * pair;
 
   const int nblk_total = (k + kBlk - 1) / kBlk;
   const int per = (nblk_total + splits - 1) / splits;
   const int blk_lo = min(nblk_total, split * per);
   const int blk_hi = min(nblk_total, blk_lo + per);
 
-  // the row's index list, with invisible or out-of-range entries marked -1
+  // this split's part of the row's index list, invisible or out-of-range entries marked -1
   const int32_t* irow = idx + i * (int64_t)k;
-  for (int j = tid; j < nblk_total * kBlk; j += blockDim.x) {
+  for (int j = blk_lo * kBlk + tid; j < blk_hi * kBlk; j += blockDim.x) {
     const int32_t s = j < k ? irow[j] : -1;
     const bool ok = s >= 0 && s <= p;
     sm.idx[j] = ok ? s : -1;
@@ -526,65 +537,106 @@ __global__ __launch_bounds__(512) void sparse_attn_pair_kernel(const uint16_t* _
 }
 
 // Merge split partials: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L.
-// Merges the split partials of one (row, head): weights 2^(m_s - M) / L per split
-// (computed once per thread, kept in registers), then every thread streams two of the
-// 512 value columns over the splits.
+// A workgroup of 256 threads takes 4 (row, head) pairs, a wave per pair; lane l streams
+// value columns 4l .. 4l+3 and 256 + 4l .. 256 + 4l + 3 (16-byte loads) over the splits.
 __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml, int n_h,
                                                                   int splits, int64_t n_q, float* __restrict__ out_f32,
                                                                   uint16_t* __restrict__ out_bf16) {
-  constexpr int kMaxSplits = 64;
-  const int64_t rh = blockIdx.x;  // (row, head)
+  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head)
+  const int lane = threadIdx.x & 63;
   const int64_t i = rh / n_h;
   const int h = (int)(rh % n_h);
   if (i >= n_q) return;
+  const float* ml = part_ml + (i * splits * (int64_t)n_h + h) * 2;
+  const int64_t mstride = (int64_t)n_h * 2;
   float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, part_ml[((i * splits + s) * n_h + h) * 2]);
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[s * mstride]);
   float L = 0.f;
-  float wgt[kMaxSplits];
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  const float* po = part_o + (i * splits * (int64_t)n_h + h) * kDv + 4 * lane;
+  const int64_t sstride = (int64_t)n_h * kDv;
+  int s = 0;
+  for (; s + 4 <= splits; s += 4) {  // four splits' loads in flight together
+    f32x4 v0[4], v1[4];
+    float wgt[4];
 #pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    wgt[s] = 0.f;
-    if (s < splits) {
-      const float ms = part_ml[((i * splits + s) * n_h + h) * 2];
-      wgt[s] = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      L += part_ml[((i * splits + s) * n_h + h) * 2 + 1] * wgt[s];
+    for (int u = 0; u < 4; ++u) {
+      v0[u] = *reinterpret_cast<const f32x4*>(po + (s + u) * sstride);
+      v1[u] = *reinterpret_cast<const f32x4*>(po + (s + u) * sstride + 256);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float ms = ml[(s + u) * mstride];
+      wgt[u] = ms == -INFINITY ? 0.f : exp2f(ms - M);
+      L = fmaf(ml[(s + u) * mstride + 1], wgt[u], L);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      a0 += v0[u] * wgt[u];
+      a1 += v1[u] * wgt[u];
+    }
+  }
+  for (; s < splits; ++s) {
+    const float ms = ml[s * mstride];
+    const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
+    L = fmaf(ml[s * mstride + 1], wgt, L);
+    a0 += *reinterpret_cast<const f32x4*>(po + s * sstride) * wgt;
+    a1 += *reinterpret_cast<const f32x4*>(po + s * sstride + 256) * wgt;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  const float* po = part_o + (i * splits * (int64_t)n_h + h) * kDv;
-  const int64_t sstride = (int64_t)n_h * kDv;
-  const int v = threadIdx.x;
-  float acc0 = 0.f, acc1 = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMaxSplits; ++s) {
-    if (s < splits) {
-      acc0 = fmaf(po[s * sstride + v], wgt[s], acc0);
-      acc1 = fmaf(po[s * sstride + v + 256], wgt[s], acc1);
-    }
-  }
-  const int64_t o = (i * n_h + h) * kDv + v;
+  a0 *= inv;
+  a1 *= inv;
+  const int64_t o = (i * n_h + h) * kDv + 4 * lane;
   if (out_f32) {
-    out_f32[o] = acc0 * inv;
-    out_f32[o + 256] = acc1 * inv;
+    *reinterpret_cast<f32x4*>(out_f32 + o) = a0;
+    *reinterpret_cast<f32x4*>(out_f32 + o + 256) = a1;
   } else {
-    out_bf16[o] = (uint16_t)f32_to_bf16_bits(acc0 * inv);
-    out_bf16[o + 256] = (uint16_t)f32_to_bf16_bits(acc1 * inv);
+    *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]));
+    *reinterpret_cast<uint2*>(out_bf16 + o + 256) = make_uint2(pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3]));
   }
 }
 
-int attn_splits(const AttnArgs& a) {
+// Work split of one call.  Prefill (many rows): one workgroup per row with every head.
+// Few rows (decode): the heads are cut into groups of 32 (two wave pairs of 16) and the
+// row's index list into splits, so that the grid has about 256 workgroups.  Each split
+// writes an fp32 partial of its heads that the combine pass merges; head groups keep that
+// partial small (64 KB per split and group at 32 heads) where a split over all 128 heads
+// would write 256 KB, and the groups of a row re-read its latent rows from one L2.
+struct AttnPlan {
+  bool paired;
+  int nw, hg, hgroups, splits;
+};
+
+AttnPlan attn_plan(const AttnArgs& a) {
+  AttnPlan pl;
   const int64_t n_q = a.seqs.q_start[a.seqs.B];
   const int nblk = (a.k + kBlk - 1) / kBlk;
-  if (n_q >= 512 || nblk <= 1) return 1;
-  // Spread few rows over about 128 workgroups.  Every split of a row writes an fp32
-  // partial of all heads (256 KB at 128 heads) that the combine pass reads back, so
-  // more splits than that cost more in partial traffic than they gain in occupancy.
-  int s = (int)((128 + n_q - 1) / n_q);
+  pl.paired = (a.n_h == 32 || a.n_h == 64 || a.n_h == 128) && a.k <= kIdxMax;
+  pl.splits = 1;
+  pl.hgroups = 1;
+  if (pl.paired) {
+    pl.hg = 2;
+    pl.nw = a.n_h / 16;
+  } else {
+    pl.hg = 1;
+    pl.nw = a.n_h / 16;
+  }
+  if (n_q >= 512 || nblk <= 1) return pl;
+  if (pl.paired) {
+    pl.hg = 1;       // a pair per 16 heads, two pairs per workgroup
+    pl.nw = 4;
+    pl.hgroups = a.n_h / 32;
+  }
+  const int64_t per_split = n_q * pl.hgroups;
+  int s = (int)((256 + per_split - 1) / per_split);
   if (s > nblk) s = nblk;
   if (s > 64) s = 64;
-  return s < 1 ? 1 : s;
+  pl.splits = s < 1 ? 1 : s;
+  return pl;
 }
+
+int attn_splits(const AttnArgs& a) { return attn_plan(a).splits; }
 
 size_t attn_ws_bytes(const AttnArgs& a) {
   const int s = attn_splits(a);
@@ -596,7 +648,8 @@ size_t attn_ws_bytes(const AttnArgs& a) {
 hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   const int64_t n_q = a.seqs.q_start[a.seqs.B];
   if (n_q == 0) return hipSuccess;
-  const int splits = attn_splits(a);
+  const AttnPlan pl = attn_plan(a);
+  const int splits = pl.splits;
   const float scale_log2 = a.scale * 1.4426950408889634f;
   float* out_f32 = a.out_dtype == DSA_FP32 ? (float*)a.out : nullptr;
   uint16_t* out_bf16 = a.out_dtype == DSA_BF16 ? (uint16_t*)a.out : nullptr;
@@ -606,33 +659,32 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
     part_o = (float*)ws;
     part_ml = part_o + (size_t)n_q * splits * a.n_h * kDv;
   }
-  dim3 grid((unsigned)(n_q * splits));
-  const bool paired = (a.n_h == 32 || a.n_h == 64 || a.n_h == 128) && a.k <= kIdxMax;
-  if (paired) {
-    // wave pairs of 32 heads: n_h / 16 waves
-#define DSA_PAIR(NWv)                                                                                            \
-  hipLaunchKernelGGL((sparse_attn_pair_kernel<2, NWv>), grid, dim3(64 * NWv), 0, st, a.q, a.latent, a.idx, a.n_h, \
-                     a.k, scale_log2, a.seqs, n_q, splits, splits == 1 ? out_f32 : nullptr,                        \
-                     splits == 1 ? out_bf16 : nullptr, part_o, part_ml)
-    if (a.n_h == 32)
-      DSA_PAIR(2);
-    else if (a.n_h == 64)
-      DSA_PAIR(4);
+  dim3 grid((unsigned)(n_q * pl.hgroups * splits));
+  float* of = splits == 1 ? out_f32 : nullptr;
+  uint16_t* ob = splits == 1 ? out_bf16 : nullptr;
+  if (pl.paired) {
+#define DSA_PAIR(HGv, NWv)                                                                                     \
+  hipLaunchKernelGGL((sparse_attn_pair_kernel<HGv, NWv>), grid, dim3(64 * NWv), 0, st, a.q, a.latent, a.idx, \
+                     a.n_h, a.k, scale_log2, a.seqs, n_q, pl.hgroups, splits, of, ob, part_o, part_ml)
+    if (pl.hg == 1 && pl.nw == 4)
+      DSA_PAIR(1, 4);
+    else if (pl.nw == 2)
+      DSA_PAIR(2, 2);
+    else if (pl.nw == 4)
+      DSA_PAIR(2, 4);
     else
-      DSA_PAIR(8);
+      DSA_PAIR(2, 8);
 #undef DSA_PAIR
   } else {
     // 16 heads per wave: the Q slice (72 VGPRs) and the O accumulator (128) stay
     // resident with two waves per SIMD and no spills.
-    const int waves = a.n_h / 16;
-    hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(64 * waves), 0, st, a.q, a.latent, a.idx, a.n_h, a.k,
-                       scale_log2, a.seqs, n_q, splits, splits == 1 ? out_f32 : nullptr,
-                       splits == 1 ? out_bf16 : nullptr, part_o, part_ml);
+    hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, dim3(64 * pl.nw), 0, st, a.q, a.latent, a.idx, a.n_h, a.k,
+                       scale_log2, a.seqs, n_q, splits, of, ob, part_o, part_ml);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3((unsigned)(n_q * a.n_h)), dim3(256), 0, st, part_o, part_ml,
-                     a.n_h, splits, n_q, out_f32, out_bf16);
+  hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3((unsigned)((n_q * a.n_h + 3) / 4)), dim3(256), 0, st, part_o,
+                     part_ml, a.n_h, splits, n_q, out_f32, out_bf16);
   return hipGetLastError();
 }
 
