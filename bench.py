@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--workload", type=int, default=4,
                     help="synthetic workload id (4 = L=200K FSSS fp8; 3 = decode B=8 over 47 layers)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement after the prefill line")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the L=32768 single-layer and L=65536 FSSSFSSS measurements after the headline")
     ap.add_argument("--L", type=int, default=None, help="override the context length (development only)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-all-f", action="store_true", help="skip the all-F comparison step")
@@ -100,6 +102,86 @@ def cpu_baseline(layers_host, roles, L, k, scale, seconds):
         done += 1
     dt = time.perf_counter() - t0
     return done / dt, done, dt, threads
+
+
+def blas_name() -> str:
+    """The BLAS library NumPy (the oracle's matrix products) was built against."""
+    try:
+        b = np.__config__.CONFIG["Build Dependencies"]["blas"]
+        return "%s %s" % (b.get("name", "?"), b.get("version", ""))
+    except Exception:  # noqa: BLE001 (older NumPy: no machine-readable config)
+        return "unknown"
+
+
+def flush_infinity_cache(buf):
+    """Overwrite a 512 MiB device buffer: evicts the 256 MB Infinity Cache (and the L2s)
+    so that a repetition does not start with the previous one's data cached."""
+    buf.fill_(1)
+
+
+def run_prefill_config(wid: int, roles: str, steps: int, warmup: int, hip, all_f: bool) -> dict:
+    """One prefill configuration timed through indexcache_forward: per-launch indexer and
+    attention times from the library's events, fractions of the MFMA peak, and (all_f) the
+    same stack with every layer F.  Work per launch as in the headline measurement."""
+    import torch
+
+    import dsa_indexer_indexcache_amd as dsa
+    import synth
+
+    wl = synth.WORKLOADS[wid]
+    L, k, dev = wl.L, wl.k, "cuda"
+    chunk = min(wl.q_chunk, 8192) if len(roles) > 1 else L
+    need_idx = "F" * len(roles) if all_f else roles
+    layers = [dsa.layer_dict(synth.workload_layer(wid, l, device=dev, with_indexer=need_idx[l] == "F"))
+              for l in range(len(roles))]
+    outs = [torch.empty((chunk, wl.n_h, 512), dtype=torch.float32, device=dev) for _ in roles]
+    icache = torch.empty((chunk, k), dtype=torch.int32, device=dev)
+    n_chunks = (L + chunk - 1) // chunk
+    torch.cuda.synchronize()
+
+    def timed(rl):
+        n_calls = n_chunks * (len(rl) + rl.count("F"))
+        ev = [hip.events(2 * n_calls) for _ in range(steps)]
+        for _ in range(warmup):
+            dsa.indexcache_forward(rl, layers, k, q_chunk=chunk, index_rows=chunk, out_rows=chunk, outs=outs,
+                                   index_cache=icache)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        traces = [dsa.indexcache_forward(rl, layers, k, q_chunk=chunk, index_rows=chunk, out_rows=chunk, outs=outs,
+                                         index_cache=icache, events=ev[s_]).trace for s_ in range(steps)]
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        ms = {0: 0.0, 1: 0.0}
+        for s_, tr in enumerate(traces):
+            for j, (kd, _, _) in enumerate(tr):
+                ms[kd] += hip.elapsed_ms(ev[s_][2 * j], ev[s_][2 * j + 1])
+        return 1e3 * wall, ms[0] / steps, ms[1] / steps
+
+    step_ms, idx_ms, attn_ms = timed(roles)
+    vis = sel = 0.0
+    for c in range(n_chunks):
+        v, s_ = pairs_in_chunk(c * chunk, min(L, (c + 1) * chunk), k)
+        vis += v
+        sel += s_
+    idx_flops = 2.0 * wl.H * wl.d * vis * roles.count("F")
+    attn_flops = wl.n_h * 2.0 * (576 + 512) * sel * len(roles)
+    peak_i = PEAK["fp8" if wl.qk_dtype == "fp8" else "bf16"]
+    res = {"workload": wl.name, "roles": roles, "q_chunk": chunk, "steps": steps, "step_ms": step_ms,
+           "indexer_topk_ms": idx_ms, "indexer_tflops": idx_flops / (idx_ms * 1e-3) / 1e12,
+           "indexer_frac": idx_flops / (idx_ms * 1e-3) / peak_i,
+           "indexer_queries_per_s": L * roles.count("F") / (idx_ms * 1e-3),
+           "sparse_attn_ms": attn_ms, "sparse_attn_tflops": attn_flops / (attn_ms * 1e-3) / 1e12,
+           "sparse_attn_frac": attn_flops / (attn_ms * 1e-3) / PEAK["bf16"],
+           "sparse_attn_tok_per_s": L * len(roles) / (attn_ms * 1e-3)}
+    if all_f:
+        f_step, f_idx, _ = timed("F" * len(roles))
+        res.update({"all_f_step_ms": f_step, "all_f_indexer_topk_ms": f_idx,
+                    "indexer_time_ratio_allF_over_pattern": f_idx / idx_ms,
+                    "step_speedup_pattern_vs_allF": f_step / step_ms,
+                    "indexer_work_saved": 1.0 - roles.count("F") / len(roles)})
+    del layers, outs, icache
+    torch.cuda.empty_cache()
+    return res
 
 
 def traffic_record(kernel_file: str, kernel: str, workload: str):
@@ -165,14 +247,18 @@ def run_decode(steps: int, warmup: int, hip, all_f: bool = True) -> dict:
         ws = res.ws
         return res
 
-    def timed(rl):
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def timed(rl, n_steps=steps):
         for _ in range(warmup):
             step(rl)
         n_ev = 2 * (len(rl) + rl.count("F"))
-        evs = [hip.events(n_ev) for _ in range(steps)]
+        evs = [hip.events(n_ev) for _ in range(n_steps)]
         traces, walls = [], []
         torch.cuda.synchronize()
-        for s_ in range(steps):      # a decode step is one synchronous latency: time each
+        for s_ in range(n_steps):    # a decode step is one synchronous latency: time each
+            flush_infinity_cache(flush)
+            torch.cuda.synchronize()
             t0 = time.perf_counter()
             traces.append(step(rl, evs[s_]).trace)
             torch.cuda.synchronize()
@@ -202,10 +288,11 @@ def run_decode(steps: int, warmup: int, hip, all_f: bool = True) -> dict:
            "indexer_bytes_per_F_layer": idx_bytes, "attn_bytes_per_layer": attn_bytes,
            "indexer_work_saved": 1.0 - n_f / len(roles)}
     if all_f:
-        ms_f, kind_f = timed("F" * len(roles))
+        ms_f, kind_f = timed("F" * len(roles), max(3, min(steps, 5)))
         res.update({"all_f_step_ms": ms_f, "step_speedup_pattern_vs_allF": ms_f / ms,
-                    "indexer_time_ratio_allF_over_pattern": float(np.sum(kind_f[0])) / float(np.sum(kind[0]))})
-    del layers, outs
+                    "indexer_time_ratio_allF_over_pattern": float(np.mean(kind_f[0])) * len(roles)
+                    / (float(np.mean(kind[0])) * n_f)})
+    del layers, outs, flush
     torch.cuda.empty_cache()
     return res
 
@@ -354,14 +441,17 @@ def main():
         allf = "F" * len(roles)
         step(allf)
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        ev_allf = hip.events(2 * n_chunks * 2 * len(roles))
-        res = step(allf, ev_allf)
-        torch.cuda.synchronize()
-        t_allf = time.perf_counter() - t1
-        idx_allf = sum(hip.elapsed_ms(ev_allf[2 * j], ev_allf[2 * j + 1])
-                       for j, (kd, _, _) in enumerate(res.trace) if kd == 0)
-        extra = {"all_f_ms_per_step": 1e3 * t_allf, "all_f_indexer_ms": idx_allf,
+        walls, idxs = [], []
+        for _ in range(3):           # three all-F steps; medians
+            ev_allf = hip.events(2 * n_chunks * 2 * len(roles))
+            t1 = time.perf_counter()
+            res = step(allf, ev_allf)
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - t1)
+            idxs.append(sum(hip.elapsed_ms(ev_allf[2 * j], ev_allf[2 * j + 1])
+                            for j, (kd, _, _) in enumerate(res.trace) if kd == 0))
+        t_allf, idx_allf = float(np.median(walls)), float(np.median(idxs))
+        extra = {"all_f_ms_per_step": 1e3 * t_allf, "all_f_indexer_ms": idx_allf, "all_f_steps": 3,
                  "indexer_time_ratio_allF_over_pattern": idx_allf / idx_ms,
                  "step_speedup_pattern_vs_allF": 1e3 * t_allf / ms_step,
                  "indexer_work_saved": 1.0 - roles.count("F") / len(roles)}
@@ -391,14 +481,17 @@ def main():
             lat_bits = synth.bits(li.latent)      # host copy before timing: the oracle reads host memory
             host["latent"].append(lambda rows, b=lat_bits: formats.decode_bf16(b[rows]))
         qps, nrows, secs, threads = cpu_baseline(host, roles, L, k, wl.scale, args.cpu_seconds)
-        cpu = {"value": qps, "unit": "queries/s", "cores": threads, "kind": "oracle",
+        cpu = {"value": qps, "unit": "queries/s", "cores": threads, "kind": "oracle", "blas": blas_name(),
                "sample": "%d query rows drawn uniformly over [0, %d) through the %s stack (fp64 NumPy indexer, "
                          "sort top-k, sparse attention), %.1f s" % (nrows, L, roles, secs)}
 
-    dec = None
+    del layers, ldicts, outs, index_cache
+    torch.cuda.empty_cache()
+    cfg1 = cfg2 = dec = None
+    if not args.no_configs and args.L is None:
+        cfg1 = run_prefill_config(1, "F", 5, 1, hip, all_f=False)
+        cfg2 = run_prefill_config(2, synth.WORKLOADS[2].roles, 3, 1, hip, all_f=not args.no_all_f)
     if not args.no_decode and args.L is None:
-        del layers, ldicts, outs, index_cache
-        torch.cuda.empty_cache()
         dec = run_decode(max(args.steps, 3), 1, hip, all_f=not args.no_all_f)
 
     line = {
@@ -418,6 +511,8 @@ def main():
     line.update(extra)
     line["index_overlap"] = overlap_line
     line["quantize_fp8_rows"] = quant_line
+    line["prefill_L32768_bf16"] = cfg1
+    line["prefill_L65536_fsssfsss"] = cfg2
     line["decode"] = dec
     print(json.dumps(line), flush=True)
 
