@@ -25,7 +25,9 @@ STATUS = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_ROLES", -3: "DSA_
 
 EXPORTS = ("dsa_indexer_topk", "dsa_indexer_topk_ws", "dsa_sparse_attn", "dsa_sparse_attn_ws",
            "indexcache_forward", "indexcache_forward_ws", "indexcache_plan", "dsa_status_string",
-           "dsa_last_error", "dsa_version", "dsa_index_overlap", "dsa_quantize_fp8_rows")
+           "dsa_last_error", "dsa_version", "dsa_index_overlap", "dsa_quantize_fp8_rows",
+           "indexcache_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class DsaError(RuntimeError):
@@ -129,6 +131,9 @@ def lib() -> ctypes.CDLL:
         L.indexcache_forward.argtypes = [ctypes.c_char_p, ctypes.POINTER(Layer), ctypes.POINTER(Shape),
                                          ctypes.POINTER(Seqs), vp, vp, vp, sz, ctypes.POINTER(Stats), vp]
         L.indexcache_forward.restype = i32
+        L.indexcache_forward_noalloc.argtypes = [ctypes.c_char_p, ctypes.POINTER(Layer), ctypes.POINTER(Shape),
+                                                 ctypes.POINTER(Seqs), vp, vp, ctypes.POINTER(Stats), vp]
+        L.indexcache_forward_noalloc.restype = i32
         L.indexcache_forward_ws.argtypes = [ctypes.c_char_p, ctypes.POINTER(Shape), ctypes.POINTER(Seqs)]
         L.indexcache_forward_ws.restype = sz
         L.indexcache_plan.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
@@ -347,14 +352,10 @@ class ForwardResult:
                       for j in range(stats.n_traced)]
 
 
-def indexcache_forward(roles: str, layers: Sequence[dict], k: int, seqs: Optional[Seqs] = None,
-                       q_chunk: Optional[int] = None, index_rows: Optional[int] = None,
-                       out_rows: Optional[int] = None, scale: Optional[float] = None, d_v: int = 512,
-                       out_dtype=torch.float32, want_scores: bool = False, outs: Optional[List[torch.Tensor]] = None,
-                       index_cache: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                       events=None, stream=None) -> ForwardResult:
-    """indexcache_forward over layers given as dicts of tensors
-    {q_idx, q_scale, k_idx, k_scale, w, q, latent} (indexer tensors needed on F layers only)."""
+def _forward_args(roles, layers, k, seqs, q_chunk, index_rows, out_rows, scale, d_v, out_dtype, want_scores, outs,
+                  index_cache, score_cache, ws, allocate: bool):
+    """Validates and marshals the arguments of indexcache_forward(_noalloc).  With
+    allocate=False every output must be given (nothing is allocated here)."""
     n_layers = len(roles)
     if len(layers) != n_layers:
         raise ValueError("one layer dict per role")
@@ -388,39 +389,84 @@ def indexcache_forward(roles: str, layers: Sequence[dict], k: int, seqs: Optiona
     shape.index_rows = int(index_rows or max(n_q, 1))
     shape.out_rows = int(out_rows or max(n_q, 1))
     if outs is None:
+        if not allocate:
+            raise ValueError("outs are required")
         outs = [torch.empty((shape.out_rows, n_h, d_v), dtype=out_dtype, device=dev) for _ in range(n_layers)]
     if len(outs) != n_layers:
         raise ValueError("one output tensor per layer")
     for l, o in enumerate(outs):
         _req(o, "outs[%d]" % l, (out_dtype,), (shape.out_rows, n_h, d_v))
     if index_cache is None:
+        if not allocate:
+            raise ValueError("index_cache is required")
         index_cache = torch.empty((shape.index_rows, k), dtype=torch.int32, device=dev)
     _req(index_cache, "index_cache", _I32, (shape.index_rows, k))
-    score_cache = torch.empty((shape.index_rows, k), dtype=torch.float32, device=dev) if want_scores else None
+    if want_scores and score_cache is None:
+        if not allocate:
+            raise ValueError("score_cache is required for want_scores")
+        score_cache = torch.empty((shape.index_rows, k), dtype=torch.float32, device=dev)
+    _req(score_cache, "score_cache", _F32, (shape.index_rows, k), optional=True)
     if ws is not None:
         _req(ws, "ws", (torch.uint8,), (None,))
     named = {"outs[%d]" % l: o for l, o in enumerate(outs)}
     for l, d in enumerate(layers):
         named.update({"layers[%d].%s" % (l, n): t for n, t in d.items() if isinstance(t, torch.Tensor)})
-    _on_gpu(index_cache=index_cache, ws=ws, **named)
+    _on_gpu(index_cache=index_cache, score_cache=score_cache, ws=ws, **named)
     arr = (Layer * n_layers)()
     for l, d in enumerate(layers):
         for name in ("q_idx", "q_scale", "k_idx", "k_scale", "w", "q", "latent"):
             t = d.get(name)
             setattr(arr[l], name, _ptr(t) if t is not None else None)
         arr[l].out = _ptr(outs[l])
-    L = lib()
-    need = L.indexcache_forward_ws(roles.encode(), ctypes.byref(shape), ctypes.byref(seqs))
-    if ws is None or ws.numel() < need:
-        ws = _workspace(need, dev)
+    return arr, shape, seqs, outs, index_cache, score_cache, dev
+
+
+def _stats(events) -> Stats:
     stats = Stats()
     if events is not None:     # ctypes array of hipEvent_t handles created by the caller
         stats.events = ctypes.cast(events, ctypes.c_void_p)
         stats.event_cap = len(events)
+    return stats
+
+
+def indexcache_forward(roles: str, layers: Sequence[dict], k: int, seqs: Optional[Seqs] = None,
+                       q_chunk: Optional[int] = None, index_rows: Optional[int] = None,
+                       out_rows: Optional[int] = None, scale: Optional[float] = None, d_v: int = 512,
+                       out_dtype=torch.float32, want_scores: bool = False, outs: Optional[List[torch.Tensor]] = None,
+                       index_cache: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                       events=None, stream=None, score_cache: Optional[torch.Tensor] = None) -> ForwardResult:
+    """indexcache_forward over layers given as dicts of tensors
+    {q_idx, q_scale, k_idx, k_scale, w, q, latent} (indexer tensors needed on F layers only)."""
+    arr, shape, seqs, outs, index_cache, score_cache, dev = _forward_args(
+        roles, layers, k, seqs, q_chunk, index_rows, out_rows, scale, d_v, out_dtype, want_scores, outs,
+        index_cache, score_cache, ws, allocate=True)
+    L = lib()
+    need = L.indexcache_forward_ws(roles.encode(), ctypes.byref(shape), ctypes.byref(seqs))
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, dev)
+    stats = _stats(events)
     _check(L.indexcache_forward(roles.encode(), arr, ctypes.byref(shape), ctypes.byref(seqs), _ptr(index_cache),
                                 _ptr(score_cache), _ptr(ws), ws.numel() if ws is not None else 0, ctypes.byref(stats),
                                 _stream(stream)))
     return ForwardResult(outs, index_cache, score_cache, stats, ws)
+
+
+def indexcache_forward_noalloc(roles: str, layers: Sequence[dict], k: int, outs: List[torch.Tensor],
+                               index_cache: torch.Tensor, seqs: Optional[Seqs] = None, q_chunk: Optional[int] = None,
+                               index_rows: Optional[int] = None, out_rows: Optional[int] = None,
+                               scale: Optional[float] = None, d_v: int = 512, out_dtype=torch.float32,
+                               score_cache: Optional[torch.Tensor] = None, events=None,
+                               stream=None) -> ForwardResult:
+    """indexcache_forward_noalloc: the same loop with the library's own per-GPU scratch array as
+    workspace; every output is passed in and nothing is allocated."""
+    arr, shape, seqs, outs, index_cache, score_cache, dev = _forward_args(
+        roles, layers, k, seqs, q_chunk, index_rows, out_rows, scale, d_v, out_dtype, score_cache is not None,
+        outs, index_cache, score_cache, None, allocate=False)
+    stats = _stats(events)
+    _check(lib().indexcache_forward_noalloc(roles.encode(), arr, ctypes.byref(shape), ctypes.byref(seqs),
+                                            _ptr(index_cache), _ptr(score_cache), ctypes.byref(stats),
+                                            _stream(stream)))
+    return ForwardResult(outs, index_cache, score_cache, stats)
 
 
 def layer_dict(li) -> dict:

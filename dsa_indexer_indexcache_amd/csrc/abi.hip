@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "../../include/dsa.h"
@@ -413,6 +414,56 @@ int indexcache_forward(const char* roles, const dsa_layer* layers, const dsa_sha
     for (int l = 0; l < n_layers; ++l) stats->src_layer[l] = src[l];
   }
   return DSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free variant of indexcache_forward.  Its workspace is this file-scope
+// device array: every GPU that runs the library holds its own copy (at its own
+// address) until the process ends.  In host code the array's name only stands in
+// for the symbol; the device address of the current device's copy is looked up
+// once per device with hipGetSymbolAddress and used from then on.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on first use).
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+}  // namespace
+
+int indexcache_forward_noalloc(const char* roles, const dsa_layer* layers, const dsa_shape* shape,
+                               const dsa_seqs* seqs, int32_t* index_cache, float* score_cache, dsa_stats* stats,
+                               void* stream) {
+  const int prc = indexcache_plan(roles, nullptr, nullptr);
+  if (prc) return prc;
+  const size_t need = indexcache_forward_ws(roles, shape, seqs);
+  if (need > (size_t)DSA_NOALLOC_SCRATCH_BYTES)
+    return fail(DSA_ERR_WORKSPACE, "this shape needs %zu bytes of workspace, above the %zu bytes of the "
+                "allocation-free entry point's scratch array", need, (size_t)DSA_NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  if (need > 0) {
+    const int rc = scratch_for_current_device(&ptr);
+    if (rc) return rc;
+  }
+  return indexcache_forward(roles, layers, shape, seqs, index_cache, score_cache, ptr,
+                            ptr ? (size_t)DSA_NOALLOC_SCRATCH_BYTES : 0, stats, stream);
 }
 
 }  // extern "C"

@@ -199,6 +199,25 @@ int indexcache_forward(const char* roles, const dsa_layer* layers /* host array 
 size_t indexcache_forward_ws(const char* roles, const dsa_shape* shape, const dsa_seqs* seqs);
 
 /*
+ * Allocation-free variant of indexcache_forward, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as indexcache_forward without
+ * ws/ws_bytes: the workspace is a file-scope device array of the library of
+ * DSA_NOALLOC_SCRATCH_BYTES per GPU, held from the library's first use on that
+ * GPU until the process ends.  Returns DSA_ERR_WORKSPACE (nothing enqueued) when
+ * indexcache_forward_ws() of the call exceeds that size.  The call allocates and
+ * frees nothing.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (different streams or threads without ordering) race; calls
+ * ordered on one stream do not.  The kernels leave no state in the array that a
+ * later call relies on.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (64u << 20) /* 64 MiB per GPU */
+int indexcache_forward_noalloc(const char* roles, const dsa_layer* layers /* host array */,
+                               const dsa_shape* shape /* host */, const dsa_seqs* seqs /* host */,
+                               int32_t* index_cache, float* score_cache, dsa_stats* stats /* host */,
+                               void* stream);
+
+/*
  * Host-only planning of the loop above ([IC] §1.1: the first layer must be F;
  * an S layer uses the nearest preceding F layer).  src_layer (host, n_layers
  * entries, may be NULL) receives max{l' <= l : roles[l'] == 'F'};

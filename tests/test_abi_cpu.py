@@ -201,3 +201,22 @@ def test_binding_rejects_bad_tensors_before_the_library():
         dsa.indexer_topk(q, kk.to(torch.float32), torch.zeros((4, 8), dtype=torch.bfloat16), 2)
     with pytest.raises(ValueError, match="x must"):
         dsa.quantize_fp8_rows(torch.zeros((4, 8), dtype=torch.float32))
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """indexcache_forward_noalloc refuses a call whose workspace exceeds its fixed
+    per-GPU array, before any launch: 64 decode rows over 400K keys need a 102 MB slab."""
+    L = dsa.lib()
+    seqs = dsa.Seqs.decode([400000] * 64)
+    shape = dsa.Shape()
+    shape.H, shape.d, shape.k, shape.n_h, shape.d_qk, shape.d_v = 64, 128, 2048, 128, 576, 512
+    shape.scale, shape.qk_dtype, shape.out_dtype = 576 ** -0.5, dsa.DSA_BF16, dsa.DSA_FP32
+    shape.q_chunk, shape.index_rows, shape.out_rows = 64, 64, 64
+    need = L.indexcache_forward_ws(b"F", ctypes.byref(shape), ctypes.byref(seqs))
+    assert need > dsa.NOALLOC_SCRATCH_BYTES
+    layers = (dsa.Layer * 1)()
+    rc = L.indexcache_forward_noalloc(b"F", layers, ctypes.byref(shape), ctypes.byref(seqs), None, None, None, None)
+    assert rc == -6
+    assert b"scratch" in L.dsa_last_error()
+    assert L.indexcache_forward_noalloc(b"SF", layers, ctypes.byref(shape), ctypes.byref(seqs), None, None, None,
+                                        None) == -3
