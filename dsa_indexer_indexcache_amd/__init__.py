@@ -26,7 +26,10 @@ STATUS = {0: "DSA_OK", -1: "DSA_ERR_INVALID_ARG", -2: "DSA_ERR_ROLES", -3: "DSA_
 EXPORTS = ("dsa_indexer_topk", "dsa_indexer_topk_ws", "dsa_sparse_attn", "dsa_sparse_attn_ws",
            "indexcache_forward", "indexcache_forward_ws", "indexcache_plan", "dsa_status_string",
            "dsa_last_error", "dsa_version", "dsa_index_overlap", "dsa_quantize_fp8_rows",
-           "indexcache_forward_noalloc")
+           "indexcache_forward_noalloc", "dsa_indexer_project", "dsa_cache_append", "dsa_attention_mass",
+           "dsa_attention_mass_ws", "dsa_indexer_kl", "dsa_indexer_kl_ws", "dsa_indexer_topk_ex",
+           "dsa_csa_compress")
+DSA_TOPK_BF16_SCORES = 1
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -38,18 +41,20 @@ class DsaError(RuntimeError):
 
 class Seqs(ctypes.Structure):
     """dsa_seqs: packed variable-length batch (see include/dsa.h)."""
-    _fields_ = [("B", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("B", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("q_start", ctypes.c_int64 * (DSA_MAX_B + 1)),
                 ("k_start", ctypes.c_int64 * (DSA_MAX_B + 1)),
                 ("q_pos0", ctypes.c_int64 * DSA_MAX_B)]
 
     @classmethod
-    def varlen(cls, q_lens: Sequence[int], k_lens: Sequence[int], q_pos0: Sequence[int]) -> "Seqs":
+    def varlen(cls, q_lens: Sequence[int], k_lens: Sequence[int], q_pos0: Sequence[int], block: int = 0) -> "Seqs":
+        """block > 1: the key rows are compressed blocks of `block` tokens (query t sees blocks s < t // block)."""
         s = cls()
         B = len(q_lens)
         if not (1 <= B <= DSA_MAX_B) or len(k_lens) != B or len(q_pos0) != B:
             raise ValueError("need 1..%d sequences with matching lengths" % DSA_MAX_B)
         s.B = B
+        s.block = int(block)
         qa = ka = 0
         for b in range(B):
             s.q_start[b] = qa
@@ -65,6 +70,12 @@ class Seqs(ctypes.Structure):
     def prefill(cls, n_q: int, n_k: Optional[int] = None, q_pos0: int = 0) -> "Seqs":
         """One sequence: n_q queries at positions q_pos0.. over n_k keys (default n_k = q_pos0 + n_q)."""
         return cls.varlen([n_q], [q_pos0 + n_q if n_k is None else n_k], [q_pos0])
+
+    @classmethod
+    def compressed(cls, n_q: int, block: int, q_pos0: int = 0, n_k: Optional[int] = None) -> "Seqs":
+        """One sequence of n_q query tokens at positions q_pos0.. over compressed blocks of `block` tokens
+        (default n_k = (q_pos0 + n_q) // block, the complete blocks of the tokens so far)."""
+        return cls.varlen([n_q], [(q_pos0 + n_q) // block if n_k is None else n_k], [q_pos0], block=block)
 
     @classmethod
     def decode(cls, lens: Iterable[int]) -> "Seqs":
@@ -91,7 +102,7 @@ class Shape(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("d", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("n_h", ctypes.c_int32), ("d_qk", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("qk_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("q_chunk", ctypes.c_int64), ("index_rows", ctypes.c_int64),
+                ("flags", ctypes.c_int32), ("q_chunk", ctypes.c_int64), ("index_rows", ctypes.c_int64),
                 ("out_rows", ctypes.c_int64)]
 
 
@@ -121,6 +132,11 @@ def lib() -> ctypes.CDLL:
         L.dsa_indexer_topk.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.POINTER(Seqs), vp, vp, vp,
                                        sz, vp]
         L.dsa_indexer_topk.restype = i32
+        L.dsa_indexer_topk_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, ctypes.POINTER(Seqs), vp, vp, vp,
+                                          sz, i32, vp]
+        L.dsa_indexer_topk_ex.restype = i32
+        L.dsa_csa_compress.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_int64, i32, i32, ctypes.c_int64, vp, i32, vp]
+        L.dsa_csa_compress.restype = i32
         L.dsa_indexer_topk_ws.argtypes = [i32, i32, i32, i32, ctypes.POINTER(Seqs)]
         L.dsa_indexer_topk_ws.restype = sz
         L.dsa_sparse_attn.argtypes = [vp, vp, vp, i32, i32, i32, i32, f32, ctypes.POINTER(Seqs), vp, i32, vp, sz,
@@ -148,6 +164,20 @@ def lib() -> ctypes.CDLL:
         L.dsa_index_overlap.restype = i32
         L.dsa_quantize_fp8_rows.argtypes = [vp, ctypes.c_int64, i32, vp, vp, vp]
         L.dsa_quantize_fp8_rows.restype = i32
+        L.dsa_indexer_project.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_int64, i32, i32, i32, i32, i32, f32,
+                                          f32, vp, vp, vp, vp]
+        L.dsa_indexer_project.restype = i32
+        L.dsa_cache_append.argtypes = [vp, ctypes.c_int64, vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
+        L.dsa_cache_append.restype = i32
+        L.dsa_attention_mass_ws.argtypes = [i32, i32, ctypes.POINTER(Seqs), i32]
+        L.dsa_attention_mass_ws.restype = sz
+        L.dsa_attention_mass.argtypes = [vp, vp, vp, i32, i32, i32, f32, ctypes.POINTER(Seqs), vp, vp, vp, vp, sz, vp]
+        L.dsa_attention_mass.restype = i32
+        L.dsa_indexer_kl_ws.argtypes = [i32, i32, ctypes.POINTER(Seqs)]
+        L.dsa_indexer_kl_ws.restype = sz
+        L.dsa_indexer_kl.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, ctypes.POINTER(Seqs), f32, i32, vp, vp, vp,
+                                     sz, vp]
+        L.dsa_indexer_kl.restype = i32
         _lib_handle = L
     return _lib_handle
 
@@ -239,8 +269,9 @@ def indexcache_plan(roles: str):
 def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, k: int, seqs: Optional[Seqs] = None,
                  q_scale: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
                  want_scores: bool = False, idx_out: Optional[torch.Tensor] = None,
-                 score_out: Optional[torch.Tensor] = None, stream=None):
-    """dsa_indexer_topk: returns (idx int32 [n_q, k], scores fp32 [n_q, k] or None)."""
+                 score_out: Optional[torch.Tensor] = None, stream=None, bf16_scores: bool = False):
+    """dsa_indexer_topk(_ex): returns (idx int32 [n_q, k], scores fp32 [n_q, k] or None).
+    bf16_scores: rank bf16-rounded scores (DSA_TOPK_BF16_SCORES)."""
     _req(q_idx, "q_idx", _QK, (None, None, None))
     n_q, H, d = q_idx.shape
     dev = q_idx.device
@@ -268,8 +299,10 @@ def indexer_topk(q_idx: torch.Tensor, k_idx: torch.Tensor, w: torch.Tensor, k: i
     L = lib()
     nbytes = L.dsa_indexer_topk_ws(dt, H, d, k, ctypes.byref(seqs))
     ws = _workspace(nbytes, dev)
-    _check(L.dsa_indexer_topk(_ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w), dt, H, d, k,
-                              ctypes.byref(seqs), _ptr(idx_out), _ptr(score_out), _ptr(ws), nbytes, _stream(stream)))
+    flags = DSA_TOPK_BF16_SCORES if bf16_scores else 0
+    _check(L.dsa_indexer_topk_ex(_ptr(q_idx), _ptr(q_scale), _ptr(k_idx), _ptr(k_scale), _ptr(w), dt, H, d, k,
+                                 ctypes.byref(seqs), _ptr(idx_out), _ptr(score_out), _ptr(ws), nbytes, flags,
+                                 _stream(stream)))
     return idx_out, score_out
 
 
@@ -339,6 +372,136 @@ def index_overlap(idx_a: torch.Tensor, idx_b: torch.Tensor, counts: Optional[tor
     return counts
 
 
+def indexer_project(q_lat: torch.Tensor, h: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor,
+                    ln_weight: torch.Tensor, ln_bias: torch.Tensor, ww: torch.Tensor, pos: torch.Tensor, H: int,
+                    rope_dim: int = 64, rope_base: float = 10000.0, eps: float = 1e-5, q_idx=None, k_idx=None,
+                    w=None, stream=None):
+    """dsa_indexer_project: (q_idx [n, H, d], k_idx [n, d], w [n, H]) bf16 from the query latent
+    q_lat [n, r] and hidden state h [n, hidden] (weights in nn.Linear layout [out, in])."""
+    _req(q_lat, "q_lat", _BF16, (None, None))
+    n, r = q_lat.shape
+    _req(h, "h", _BF16, (n, None))
+    hidden = h.shape[1]
+    _req(wk, "wk", _BF16, (None, hidden))
+    d = wk.shape[0]
+    _req(wq, "wq", _BF16, (H * d, r))
+    _req(ww, "ww", _BF16, (H, hidden))
+    _req(ln_weight, "ln_weight", _F32, (d,))
+    _req(ln_bias, "ln_bias", _F32, (d,))
+    _req(pos, "pos", _I32, (n,))
+    dev = q_lat.device
+    if q_idx is None:
+        q_idx = torch.empty((n, H, d), dtype=torch.bfloat16, device=dev)
+    if k_idx is None:
+        k_idx = torch.empty((n, d), dtype=torch.bfloat16, device=dev)
+    if w is None:
+        w = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+    _req(q_idx, "q_idx", _BF16, (n, H, d))
+    _req(k_idx, "k_idx", _BF16, (n, d))
+    _req(w, "w", _BF16, (n, H))
+    _on_gpu(q_lat=q_lat, h=h, wq=wq, wk=wk, ln_weight=ln_weight, ln_bias=ln_bias, ww=ww, pos=pos, q_idx=q_idx,
+            k_idx=k_idx, w=w)
+    _check(lib().dsa_indexer_project(_ptr(q_lat), _ptr(h), _ptr(wq), _ptr(wk), _ptr(ln_weight), _ptr(ln_bias),
+                                     _ptr(ww), _ptr(pos), n, r, hidden, H, d, rope_dim, float(rope_base), float(eps),
+                                     _ptr(q_idx), _ptr(k_idx), _ptr(w), _stream(stream)))
+    return q_idx, k_idx, w
+
+
+def _stat_inputs(q, latent, idx, seqs):
+    _req(q, "q", _BF16, (None, None, None))
+    n_q, n_h, d_qk = q.shape
+    _req(latent, "latent", _BF16, (None, d_qk))
+    _req(idx, "idx", _I32, (n_q, None))
+    if seqs is None:
+        seqs = Seqs.prefill(n_q, latent.shape[0], q_pos0=latent.shape[0] - n_q)
+    if seqs.n_q != n_q or seqs.n_k > latent.shape[0]:
+        raise ValueError("seqs describes %d queries over %d keys; tensors hold %d and %d"
+                         % (seqs.n_q, seqs.n_k, n_q, latent.shape[0]))
+    return n_q, n_h, d_qk, idx.shape[1], seqs
+
+
+def attention_mass(q: torch.Tensor, latent: torch.Tensor, idx: torch.Tensor, seqs: Optional[Seqs] = None,
+                   scale: Optional[float] = None, want_recall: bool = True, stream=None):
+    """dsa_attention_mass: (mass_head [n_q, n_h], mass [n_q], recall [n_q] or None), fp32:
+    CapturedMass@k per head and for the head-aggregated dense distribution, Recall@k of
+    the selection idx against the dense distribution's own top-k."""
+    n_q, n_h, d_qk, k, seqs = _stat_inputs(q, latent, idx, seqs)
+    dev = q.device
+    mass_head = torch.empty((n_q, n_h), dtype=torch.float32, device=dev)
+    mass = torch.empty((n_q,), dtype=torch.float32, device=dev)
+    recall = torch.empty((n_q,), dtype=torch.float32, device=dev) if want_recall else None
+    _on_gpu(q=q, latent=latent, idx=idx)
+    L = lib()
+    nbytes = L.dsa_attention_mass_ws(n_h, k, ctypes.byref(seqs), int(want_recall))
+    ws = _workspace(nbytes, dev)
+    _check(L.dsa_attention_mass(_ptr(q), _ptr(latent), _ptr(idx), n_h, d_qk, k,
+                                float(d_qk ** -0.5 if scale is None else scale), ctypes.byref(seqs), _ptr(mass_head),
+                                _ptr(mass), _ptr(recall), _ptr(ws), nbytes, _stream(stream)))
+    return mass_head, mass, recall
+
+
+def indexer_kl(q: torch.Tensor, latent: torch.Tensor, idx: torch.Tensor, scores: torch.Tensor,
+               seqs: Optional[Seqs] = None, scale: Optional[float] = None, weight: float = 1.0,
+               kl: Optional[torch.Tensor] = None, accumulate: bool = False, want_loss: bool = False, stream=None):
+    """dsa_indexer_kl: per-row KL(p_{t,S_t} || softmax(I_{t,S_t})) (times weight, added to kl
+    when accumulate), and optionally the sum over rows (a 1-element tensor)."""
+    n_q, n_h, d_qk, k, seqs = _stat_inputs(q, latent, idx, seqs)
+    _req(scores, "scores", _F32, (n_q, k))
+    dev = q.device
+    if kl is None:
+        if accumulate:
+            raise ValueError("accumulate needs the kl tensor to add to")
+        kl = torch.empty((n_q,), dtype=torch.float32, device=dev)
+    _req(kl, "kl", _F32, (n_q,))
+    loss = torch.empty((1,), dtype=torch.float32, device=dev) if want_loss else None
+    _on_gpu(q=q, latent=latent, idx=idx, scores=scores, kl=kl)
+    L = lib()
+    nbytes = L.dsa_indexer_kl_ws(n_h, k, ctypes.byref(seqs))
+    ws = _workspace(nbytes, dev)
+    _check(L.dsa_indexer_kl(_ptr(q), _ptr(latent), _ptr(idx), _ptr(scores), n_h, d_qk, k,
+                            float(d_qk ** -0.5 if scale is None else scale), ctypes.byref(seqs), float(weight),
+                            int(accumulate), _ptr(kl), _ptr(loss), _ptr(ws), nbytes, _stream(stream)))
+    return kl, loss
+
+
+def csa_compress(ca: torch.Tensor, cb: torch.Tensor, za: torch.Tensor, zb: torch.Tensor, ba: torch.Tensor,
+                 bb: torch.Tensor, m: int, block0: int = 0, out: Optional[torch.Tensor] = None,
+                 out_dtype=torch.bfloat16, stream=None) -> torch.Tensor:
+    """dsa_csa_compress: gated pooling of the n token rows into compressed entries block0 .. n // m - 1.
+    ca, cb, za, zb [n, c] bf16; ba, bb [m, c] fp32; returns out [n // m - block0, c]."""
+    _req(ca, "ca", _BF16, (None, None))
+    n, c = ca.shape
+    for name, t in (("cb", cb), ("za", za), ("zb", zb)):
+        _req(t, name, _BF16, (n, c))
+    _req(ba, "ba", _F32, (m, c))
+    _req(bb, "bb", _F32, (m, c))
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be float32 or bfloat16")
+    n_out = max(n // m - block0, 0) if m >= 1 else 0
+    if out is None:
+        out = torch.empty((n_out, c), dtype=out_dtype, device=ca.device)
+    _req(out, "out", (out_dtype,), (n_out, c))
+    _on_gpu(ca=ca, cb=cb, za=za, zb=zb, ba=ba, bb=bb, out=out)
+    _check(lib().dsa_csa_compress(_ptr(ca), _ptr(cb), _ptr(za), _ptr(zb), _ptr(ba), _ptr(bb), n, c, m, block0,
+                                  _ptr(out), DSA_FP32 if out_dtype == torch.float32 else DSA_BF16,
+                                  _stream(stream)))
+    return out
+
+
+def cache_append(cache: torch.Tensor, dst_row: torch.Tensor, rows: torch.Tensor, stream=None) -> torch.Tensor:
+    """dsa_cache_append: rows[b] -> cache[dst_row[b]] (2-D tensors of one dtype and row width;
+    dst_row int64).  Destinations outside the cache are skipped."""
+    if not isinstance(cache, torch.Tensor) or cache.dim() != 2:
+        raise ValueError("cache must be a 2-D tensor")
+    _req(cache, "cache", (cache.dtype,), tuple(cache.shape))
+    _req(rows, "rows", (cache.dtype,), (None, cache.shape[1]))
+    _req(dst_row, "dst_row", (torch.int64,), (rows.shape[0],))
+    _on_gpu(cache=cache, dst_row=dst_row, rows=rows)
+    _check(lib().dsa_cache_append(_ptr(cache), cache.shape[0], _ptr(dst_row), _ptr(rows), rows.shape[0],
+                                  cache.shape[1] * cache.element_size(), _stream(stream)))
+    return cache
+
+
 class ForwardResult:
     def __init__(self, outs, index_cache, score_cache, stats: Stats, ws=None):
         self.outs = outs
@@ -353,7 +516,7 @@ class ForwardResult:
 
 
 def _forward_args(roles, layers, k, seqs, q_chunk, index_rows, out_rows, scale, d_v, out_dtype, want_scores, outs,
-                  index_cache, score_cache, ws, allocate: bool):
+                  index_cache, score_cache, ws, allocate: bool, bf16_scores: bool = False):
     """Validates and marshals the arguments of indexcache_forward(_noalloc).  With
     allocate=False every output must be given (nothing is allocated here)."""
     n_layers = len(roles)
@@ -385,6 +548,7 @@ def _forward_args(roles, layers, k, seqs, q_chunk, index_rows, out_rows, scale, 
     shape.scale = float(d_qk ** -0.5 if scale is None else scale)
     shape.qk_dtype = _dtype_code(qi) if qi is not None else DSA_BF16
     shape.out_dtype = DSA_FP32 if out_dtype == torch.float32 else DSA_BF16
+    shape.flags = DSA_TOPK_BF16_SCORES if bf16_scores else 0
     shape.q_chunk = int(q_chunk or max(n_q, 1))
     shape.index_rows = int(index_rows or max(n_q, 1))
     shape.out_rows = int(out_rows or max(n_q, 1))
@@ -434,12 +598,14 @@ def indexcache_forward(roles: str, layers: Sequence[dict], k: int, seqs: Optiona
                        out_rows: Optional[int] = None, scale: Optional[float] = None, d_v: int = 512,
                        out_dtype=torch.float32, want_scores: bool = False, outs: Optional[List[torch.Tensor]] = None,
                        index_cache: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                       events=None, stream=None, score_cache: Optional[torch.Tensor] = None) -> ForwardResult:
+                       events=None, stream=None, score_cache: Optional[torch.Tensor] = None,
+                       bf16_scores: bool = False) -> ForwardResult:
     """indexcache_forward over layers given as dicts of tensors
-    {q_idx, q_scale, k_idx, k_scale, w, q, latent} (indexer tensors needed on F layers only)."""
+    {q_idx, q_scale, k_idx, k_scale, w, q, latent} (indexer tensors needed on F layers only).
+    bf16_scores: the F layers rank bf16-rounded scores (DSA_TOPK_BF16_SCORES)."""
     arr, shape, seqs, outs, index_cache, score_cache, dev = _forward_args(
         roles, layers, k, seqs, q_chunk, index_rows, out_rows, scale, d_v, out_dtype, want_scores, outs,
-        index_cache, score_cache, ws, allocate=True)
+        index_cache, score_cache, ws, allocate=True, bf16_scores=bf16_scores)
     L = lib()
     need = L.indexcache_forward_ws(roles.encode(), ctypes.byref(shape), ctypes.byref(seqs))
     if ws is None or ws.numel() < need:
@@ -456,12 +622,12 @@ def indexcache_forward_noalloc(roles: str, layers: Sequence[dict], k: int, outs:
                                index_rows: Optional[int] = None, out_rows: Optional[int] = None,
                                scale: Optional[float] = None, d_v: int = 512, out_dtype=torch.float32,
                                score_cache: Optional[torch.Tensor] = None, events=None,
-                               stream=None) -> ForwardResult:
+                               stream=None, bf16_scores: bool = False) -> ForwardResult:
     """indexcache_forward_noalloc: the same loop with the library's own per-GPU scratch array as
     workspace; every output is passed in and nothing is allocated."""
     arr, shape, seqs, outs, index_cache, score_cache, dev = _forward_args(
         roles, layers, k, seqs, q_chunk, index_rows, out_rows, scale, d_v, out_dtype, score_cache is not None,
-        outs, index_cache, score_cache, None, allocate=False)
+        outs, index_cache, score_cache, None, allocate=False, bf16_scores=bf16_scores)
     stats = _stats(events)
     _check(lib().indexcache_forward_noalloc(roles.encode(), arr, ctypes.byref(shape), ctypes.byref(seqs),
                                             _ptr(index_cache), _ptr(score_cache), ctypes.byref(stats),

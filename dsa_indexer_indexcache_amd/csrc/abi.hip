@@ -38,14 +38,16 @@ int check_seqs(const dsa_seqs* s, int64_t* n_q, int64_t* n_k) {
   if (s->B < 1 || s->B > DSA_MAX_B) return fail(DSA_ERR_INVALID_ARG, "seqs->B=%d outside [1,%d]", s->B, DSA_MAX_B);
   if (s->q_start[0] != 0) return fail(DSA_ERR_INVALID_ARG, "seqs->q_start[0] must be 0");
   if (s->k_start[0] < 0) return fail(DSA_ERR_INVALID_ARG, "seqs->k_start[0] < 0");
+  if (s->block < 0 || s->block > (1 << 20)) return fail(DSA_ERR_INVALID_ARG, "seqs->block=%d", s->block);
   for (int b = 0; b < s->B; ++b) {
     const int64_t nq = s->q_start[b + 1] - s->q_start[b];
     const int64_t nk = s->k_start[b + 1] - s->k_start[b];
     if (nq < 0 || nk < 0) return fail(DSA_ERR_INVALID_ARG, "sequence %d: decreasing row offsets", b);
     if (s->q_pos0[b] < 0) return fail(DSA_ERR_INVALID_ARG, "sequence %d: q_pos0 < 0", b);
-    if (nq > 0 && s->q_pos0[b] + nq > nk)
+    const int64_t need = s->block > 1 ? (s->q_pos0[b] + nq - 1) / s->block : s->q_pos0[b] + nq;
+    if (nq > 0 && need > nk)
       return fail(DSA_ERR_INVALID_ARG, "sequence %d: last query position %lld needs %lld keys, has %lld", b,
-                  (long long)(s->q_pos0[b] + nq - 1), (long long)(s->q_pos0[b] + nq), (long long)nk);
+                  (long long)(s->q_pos0[b] + nq - 1), (long long)need, (long long)nk);
     if (s->q_pos0[b] + nq > (int64_t)INT32_MAX)
       return fail(DSA_ERR_INVALID_ARG, "sequence %d: positions exceed int32", b);
   }
@@ -126,6 +128,7 @@ dsa::IndexerArgs indexer_args(const void* q_idx, const float* q_scale, const voi
   a.seqs = s;
   a.idx_out = idx_out;
   a.score_out = score_out;
+  a.flags = 0;
   return a;
 }
 
@@ -187,6 +190,7 @@ dsa_seqs slice_seqs(const dsa_seqs& s, int64_t r0, int64_t r1) {
     nb = 1;
   }
   o.B = nb;
+  o.block = s.block;
   return o;
 }
 
@@ -218,6 +222,158 @@ int dsa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows
   if (!idx_a || !idx_b || !counts) return fail(DSA_ERR_INVALID_ARG, "null pointer");
   hipError_t e = dsa::launch_index_overlap(idx_a, idx_b, n_rows, k, counts, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "index overlap launch");
+  return DSA_OK;
+}
+
+int dsa_indexer_project(const uint16_t* q_lat, const uint16_t* h, const uint16_t* wq, const uint16_t* wk,
+                        const float* ln_weight, const float* ln_bias, const uint16_t* ww, const int32_t* pos, int64_t n,
+                        int r, int hidden, int H, int d, int rope_dim, float rope_base, float eps, uint16_t* q_idx,
+                        uint16_t* k_idx, uint16_t* w, void* stream) {
+  if (n < 0) return fail(DSA_ERR_INVALID_ARG, "n=%lld < 0", (long long)n);
+  if (d != 128) return fail(DSA_ERR_UNSUPPORTED, "indexer head dim d=%d: only 128 is compiled", d);
+  if (H < 1 || H > 128) return fail(DSA_ERR_UNSUPPORTED, "indexer heads H=%d outside [1, 128]", H);
+  if (rope_dim != 0 && rope_dim != 32 && rope_dim != 64)
+    return fail(DSA_ERR_UNSUPPORTED, "rope_dim=%d not in {0, 32, 64}", rope_dim);
+  if (r < 64 || r % 64 || hidden < 64 || hidden % 64)
+    return fail(DSA_ERR_UNSUPPORTED, "r=%d and hidden=%d must be positive multiples of 64", r, hidden);
+  if (!(rope_base > 1.f) || !(eps >= 0.f)) return fail(DSA_ERR_INVALID_ARG, "rope_base must exceed 1, eps >= 0");
+  if (n > (int64_t)INT32_MAX * 64) return fail(DSA_ERR_UNSUPPORTED, "n=%lld too large", (long long)n);
+  if (n == 0) return DSA_OK;
+  if (!q_lat || !h || !wq || !wk || !ln_weight || !ln_bias || !ww || !pos || !q_idx || !k_idx || !w)
+    return fail(DSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(q_lat) || !aligned16(h) || !aligned16(wq) || !aligned16(wk) || !aligned16(ww) ||
+      !aligned16(q_idx) || !aligned16(k_idx))
+    return fail(DSA_ERR_ALIGNMENT, "q_lat, h, the weights, q_idx and k_idx must be 16-byte aligned");
+  if (((uintptr_t)w & 1u) || ((uintptr_t)pos & 3u) || ((uintptr_t)ln_weight & 3u) || ((uintptr_t)ln_bias & 3u))
+    return fail(DSA_ERR_ALIGNMENT, "w, pos or the LayerNorm parameters misaligned");
+  dsa::ProjectArgs a{q_lat, h, wq, wk, ln_weight, ln_bias, ww, pos, n, r, hidden, H, rope_dim, rope_base, eps,
+                     q_idx, k_idx, w};
+  hipError_t e = dsa::launch_indexer_project(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer projection launch");
+  return DSA_OK;
+}
+
+int dsa_cache_append(void* cache, int64_t cache_rows, const int64_t* dst_row, const void* rows, int64_t n_rows,
+                     int64_t row_bytes, void* stream) {
+  if (n_rows < 0 || cache_rows < 0 || row_bytes < 1) return fail(DSA_ERR_INVALID_ARG, "negative size");
+  if (n_rows > INT32_MAX) return fail(DSA_ERR_UNSUPPORTED, "n_rows=%lld > 2^31 - 1", (long long)n_rows);
+  if (n_rows == 0) return DSA_OK;
+  if (!cache || !dst_row || !rows) return fail(DSA_ERR_INVALID_ARG, "null pointer");
+  if ((uintptr_t)dst_row & 7u) return fail(DSA_ERR_ALIGNMENT, "dst_row misaligned");
+  hipError_t e = dsa::launch_cache_append(cache, cache_rows, dst_row, rows, n_rows, row_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "cache append launch");
+  return DSA_OK;
+}
+
+int dsa_csa_compress(const uint16_t* ca, const uint16_t* cb, const uint16_t* za, const uint16_t* zb,
+                     const float* ba, const float* bb, int64_t n, int c, int m, int64_t block0, void* out,
+                     int out_dtype, void* stream) {
+  if (n < 0 || block0 < 0) return fail(DSA_ERR_INVALID_ARG, "n=%lld block0=%lld", (long long)n, (long long)block0);
+  if (c < 8 || c % 8) return fail(DSA_ERR_UNSUPPORTED, "c=%d is not a positive multiple of 8", c);
+  if (m < 1 || m > 4096) return fail(DSA_ERR_UNSUPPORTED, "m=%d outside 1..4096", m);
+  if (out_dtype != DSA_FP32 && out_dtype != DSA_BF16) return fail(DSA_ERR_INVALID_ARG, "out_dtype=%d", out_dtype);
+  const int64_t n_out = n / m - block0;
+  if (n_out <= 0) return DSA_OK;
+  if (n_out * (c / 8) > ((int64_t)UINT32_MAX) * 256 / 2)
+    return fail(DSA_ERR_UNSUPPORTED, "%lld entries of %d columns exceed one launch", (long long)n_out, c);
+  if (!ca || !cb || !za || !zb || !ba || !bb || !out) return fail(DSA_ERR_INVALID_ARG, "null pointer");
+  if (!aligned16(ca) || !aligned16(cb) || !aligned16(za) || !aligned16(zb) || !aligned16(ba) || !aligned16(bb) ||
+      !aligned16(out))
+    return fail(DSA_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  dsa::CsaArgs a;
+  a.ca = ca;
+  a.cb = cb;
+  a.za = za;
+  a.zb = zb;
+  a.ba = ba;
+  a.bb = bb;
+  a.n = n;
+  a.block0 = block0;
+  a.c = c;
+  a.m = m;
+  a.out = out;
+  a.out_dtype = out_dtype;
+  hipError_t e = dsa::launch_csa_compress(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "csa compress launch");
+  return DSA_OK;
+}
+
+static int check_stats(const uint16_t* q, const uint16_t* latent, const int32_t* idx, int n_h, int d_qk, int k,
+                       int64_t n_q) {
+  if (k < 1) return fail(DSA_ERR_INVALID_ARG, "k=%d < 1", k);
+  if (n_h != 16 && n_h != 32 && n_h != 64 && n_h != 128)
+    return fail(DSA_ERR_UNSUPPORTED, "n_h=%d not in {16,32,64,128}", n_h);
+  if (d_qk != 576) return fail(DSA_ERR_UNSUPPORTED, "needs d_qk=576 (got %d)", d_qk);
+  if (k > 2048) return fail(DSA_ERR_UNSUPPORTED, "k=%d > 2048", k);
+  if (n_q == 0) return DSA_OK;
+  if (!q || !latent || !idx) return fail(DSA_ERR_INVALID_ARG, "q, latent and idx are required");
+  if (!aligned16(q) || !aligned16(latent) || ((uintptr_t)idx & 3u))
+    return fail(DSA_ERR_ALIGNMENT, "q/latent not 16-byte aligned or idx misaligned");
+  return DSA_OK;
+}
+
+static dsa::StatArgs stat_args(const uint16_t* q, const uint16_t* latent, const int32_t* idx, int n_h, int k,
+                               float scale, const dsa_seqs& s) {
+  dsa::StatArgs a;
+  a.q = q;
+  a.latent = latent;
+  a.idx = idx;
+  a.n_h = n_h;
+  a.k = k;
+  a.scale = scale;
+  a.seqs = s;
+  return a;
+}
+
+size_t dsa_attention_mass_ws(int n_h, int k, const dsa_seqs* seqs, int want_recall) {
+  int64_t n_q, n_k;
+  if (check_seqs(seqs, &n_q, &n_k) != DSA_OK) return 0;
+  return dsa::attn_mass_ws(stat_args(nullptr, nullptr, nullptr, n_h, k, 1.f, *seqs), want_recall != 0);
+}
+
+int dsa_attention_mass(const uint16_t* q, const uint16_t* latent, const int32_t* idx, int n_h, int d_qk, int k,
+                       float scale, const dsa_seqs* seqs, float* mass_head, float* mass, float* recall, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int64_t n_q, n_k;
+  int rc = check_seqs(seqs, &n_q, &n_k);
+  if (rc) return rc;
+  rc = check_stats(q, latent, idx, n_h, d_qk, k, n_q);
+  if (rc) return rc;
+  if (n_q == 0) return DSA_OK;
+  if (!mass) return fail(DSA_ERR_INVALID_ARG, "mass is required");
+  if (((uintptr_t)mass & 3u) || ((uintptr_t)mass_head & 3u) || ((uintptr_t)recall & 3u))
+    return fail(DSA_ERR_ALIGNMENT, "outputs misaligned");
+  const dsa::StatArgs a = stat_args(q, latent, idx, n_h, k, scale, *seqs);
+  const size_t need = dsa::attn_mass_ws(a, recall != nullptr);
+  if (ws_bytes < need || !ws) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipError_t e = dsa::launch_attention_mass(a, mass_head, mass, recall, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "attention mass launch");
+  return DSA_OK;
+}
+
+size_t dsa_indexer_kl_ws(int n_h, int k, const dsa_seqs* seqs) {
+  int64_t n_q, n_k;
+  if (check_seqs(seqs, &n_q, &n_k) != DSA_OK) return 0;
+  return dsa::indexer_kl_ws(stat_args(nullptr, nullptr, nullptr, n_h, k, 1.f, *seqs));
+}
+
+int dsa_indexer_kl(const uint16_t* q, const uint16_t* latent, const int32_t* idx, const float* scores, int n_h,
+                   int d_qk, int k, float scale, const dsa_seqs* seqs, float weight, int accumulate, float* kl,
+                   float* loss, void* ws, size_t ws_bytes, void* stream) {
+  int64_t n_q, n_k;
+  int rc = check_seqs(seqs, &n_q, &n_k);
+  if (rc) return rc;
+  rc = check_stats(q, latent, idx, n_h, d_qk, k, n_q);
+  if (rc) return rc;
+  if (n_q == 0) return DSA_OK;
+  if (!scores || !kl) return fail(DSA_ERR_INVALID_ARG, "scores and kl are required");
+  if (((uintptr_t)scores & 3u) || ((uintptr_t)kl & 3u) || ((uintptr_t)loss & 3u))
+    return fail(DSA_ERR_ALIGNMENT, "scores/kl/loss misaligned");
+  const dsa::StatArgs a = stat_args(q, latent, idx, n_h, k, scale, *seqs);
+  const size_t need = dsa::indexer_kl_ws(a);
+  if (ws_bytes < need || !ws) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  hipError_t e = dsa::launch_indexer_kl(a, scores, weight, accumulate, kl, loss, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "indexer KL launch");
   return DSA_OK;
 }
 
@@ -265,6 +421,14 @@ size_t dsa_indexer_topk_ws(int qk_dtype, int H, int d, int k, const dsa_seqs* se
 int dsa_indexer_topk(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
                      const uint16_t* w, int qk_dtype, int H, int d, int k, const dsa_seqs* seqs, int32_t* idx_out,
                      float* score_out, void* ws, size_t ws_bytes, void* stream) {
+  return dsa_indexer_topk_ex(q_idx, q_scale, k_idx, k_scale, w, qk_dtype, H, d, k, seqs, idx_out, score_out, ws,
+                             ws_bytes, 0, stream);
+}
+
+int dsa_indexer_topk_ex(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
+                        const uint16_t* w, int qk_dtype, int H, int d, int k, const dsa_seqs* seqs, int32_t* idx_out,
+                        float* score_out, void* ws, size_t ws_bytes, int flags, void* stream) {
+  if (flags & ~DSA_TOPK_BF16_SCORES) return fail(DSA_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   int64_t n_q, n_k;
   int rc = check_seqs(seqs, &n_q, &n_k);
   if (rc) return rc;
@@ -275,8 +439,9 @@ int dsa_indexer_topk(const void* q_idx, const float* q_scale, const void* k_idx,
   if (((uintptr_t)idx_out & 3u) || ((uintptr_t)score_out & 3u)) return fail(DSA_ERR_ALIGNMENT, "outputs misaligned");
   const size_t need = indexer_ws(n_q, *seqs, qk_dtype, H, d, k);
   if (ws_bytes < need || (need && !ws)) return fail(DSA_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-  return run_indexer(indexer_args(q_idx, q_scale, k_idx, k_scale, w, qk_dtype, H, d, k, *seqs, idx_out, score_out),
-                     ws, (hipStream_t)stream);
+  dsa::IndexerArgs a = indexer_args(q_idx, q_scale, k_idx, k_scale, w, qk_dtype, H, d, k, *seqs, idx_out, score_out);
+  a.flags = flags;
+  return run_indexer(a, ws, (hipStream_t)stream);
 }
 
 size_t dsa_sparse_attn_ws(int n_h, int d_qk, int d_v, int k, const dsa_seqs* seqs) {
@@ -341,6 +506,7 @@ int indexcache_forward(const char* roles, const dsa_layer* layers, const dsa_sha
   rc = check_seqs(seqs, &n_q, &n_k);
   if (rc) return rc;
   if (shape->q_chunk < 1) return fail(DSA_ERR_INVALID_ARG, "q_chunk < 1");
+  if (shape->flags & ~DSA_TOPK_BF16_SCORES) return fail(DSA_ERR_INVALID_ARG, "unknown flags 0x%x", shape->flags);
   if (n_q > 0 && !index_cache) return fail(DSA_ERR_INVALID_ARG, "index_cache is required");
   for (int l = 0; l < n_layers; ++l) {
     const dsa_layer& L = layers[l];
@@ -392,6 +558,7 @@ int indexcache_forward(const char* roles, const dsa_layer* layers, const dsa_sha
                                           L.q_scale ? L.q_scale + r0 * shape->H : nullptr, L.k_idx, L.k_scale,
                                           L.w + r0 * shape->H, shape->qk_dtype, shape->H, shape->d, shape->k, cs,
                                           icache, scache);
+        a.flags = shape->flags;
         const bool tr = trace_begin(0, l, n_chunks);
         rc = run_indexer(a, ws, st);
         if (rc) return fail(rc, "layer %d chunk %d: %s", l, n_chunks, g_last_error.c_str());

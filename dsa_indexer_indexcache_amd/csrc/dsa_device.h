@@ -88,6 +88,35 @@ __device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {
       : "memory");
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// (lgkmcnt), not for outstanding global->LDS copies (vmcnt).  The "memory"
+// clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// max over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48), all lanes get it
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48), all lanes get it.
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Last key row visible to packed query row i of sequence b (sequence-local): its token
+// position t in token mode (s <= t), floor(t / block) - 1 with a compression ratio
+// block > 1 (compressed block s is visible iff s < floor(t / block); -1: none).
+__device__ __forceinline__ int64_t row_last(const dsa_seqs& s, int b, int64_t i) {
+  const int64_t t = s.q_pos0[b] + (i - s.q_start[b]);
+  return s.block > 1 ? t / s.block - 1 : t;
+}
+
 // Locate the sequence that owns packed query row i (wave-uniform; the table is
 // a kernel argument, so this is a short scalar loop).
 __device__ __forceinline__ int seq_of_row(const dsa_seqs& s, int64_t i) {

@@ -220,7 +220,8 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
                                                              const float* __restrict__ k_scale,
                                                              const uint16_t* __restrict__ w, int H, int k,
                                                              int64_t n_q, int64_t q_pos0, int64_t k_row0,
-                                                             int64_t n_keys, int32_t* __restrict__ idx_out,
+                                                             int64_t n_keys, int block, int bf16_scores,
+                                                             int32_t* __restrict__ idx_out,
                                                              float* __restrict__ score_out) {
   using C = FCfg<FP8, D>;
   constexpr int kRing = ring_of<FP8, D>();
@@ -232,8 +233,11 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
   const int64_t i0 = grp * kFW;
   const int64_t i = i0 + wave;
   const bool row_ok = i < n_q;
-  const int64_t t = row_ok ? q_pos0 + i : -1;                         // this wave's position
-  const int64_t t_max = q_pos0 + (i0 + kFW - 1 < n_q ? i0 + kFW - 1 : n_q - 1);
+  // last visible key of a row: its position, or its last visible compressed block
+  // (floor(t / block) - 1, -1 for none) with block > 1
+  auto last_key = [&](int64_t r) { return block > 1 ? (q_pos0 + r) / block - 1 : q_pos0 + r; };
+  const int64_t t = row_ok ? last_key(i) : -1;
+  const int64_t t_max = last_key(i0 + kFW - 1 < n_q ? i0 + kFW - 1 : n_q - 1);
   constexpr int kTK = FCfg<FP8, D>::tile_keys;
   const int n_tiles = (int)((t_max + kTK) / kTK);
   const uint8_t* kbytes = (const uint8_t*)k_idx + k_row0 * C::row_bytes;
@@ -383,6 +387,7 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
       const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(s02), __float_as_uint(s13), false, false);
       float score = __uint_as_float(y[0]) + __uint_as_float(y[1]);
       if constexpr (FP8) score *= sm.kscale[bi][kFT * sub + lane];
+      if (bf16_scores) score = __uint_as_float(f32_to_bf16_bits(score) << 16);
 
       // ---- filter into the pending list
       const int64_t s = (int64_t)T * kTK + kFT * sub + lane;
@@ -514,7 +519,7 @@ hipError_t launch_indexer_fused(const IndexerArgs& a, hipStream_t st) {
   if (HB == HBv && fp8 == F8 && a.d == Dv) {                                                                  \
     hipLaunchKernelGGL((idx_topk_fused_kernel<HBv, F8, Dv>), grid, dim3(64 * kFW), 0, st, a.q_idx, a.q_scale,   \
                        a.k_idx, a.k_scale, a.w, a.H, a.k, n_q, a.seqs.q_pos0[0], a.seqs.k_start[0], n_keys,  \
-                       a.idx_out, a.score_out);                                                              \
+                       a.seqs.block, a.flags & DSA_TOPK_BF16_SCORES, a.idx_out, a.score_out);                \
     found = true;                                                                                            \
   }
   bool found = false;

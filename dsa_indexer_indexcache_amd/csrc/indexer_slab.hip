@@ -26,12 +26,13 @@ template <int HB, int D>
 __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __restrict__ q_idx,
                                                              const uint16_t* __restrict__ k_idx,
                                                              const uint16_t* __restrict__ w, int H, dsa_seqs seqs,
-                                                             int64_t n_q, float* __restrict__ slab, int64_t ld) {
+                                                             int64_t n_q, float* __restrict__ slab, int64_t ld,
+                                                             int bf16_scores) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t i = (int64_t)blockIdx.y * 4 + wave;
   if (i >= n_q) return;
   const int b = seq_of_row(seqs, i);
-  const int64_t p = seqs.q_pos0[b] + (i - seqs.q_start[b]);
+  const int64_t p = row_last(seqs, b, i);
   const int64_t s0 = (int64_t)blockIdx.x * kScoreKeysPerWave;
   if (s0 > p) return;
   const int64_t krow0 = seqs.k_start[b];
@@ -82,6 +83,7 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
     const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
     part = __uint_as_float(y[0]) + __uint_as_float(y[1]);
     const int64_t s = s0 + 16 * sb + c;
+    if (bf16_scores) part = __uint_as_float(f32_to_bf16_bits(part) << 16);
     if (g == 0 && s <= p) slab[i * ld + s] = part;
   };
   i32x4 bfa[KS], bfb[KS];
@@ -104,13 +106,14 @@ __global__ __launch_bounds__(256) void idx_score_fp8_kernel(const uint8_t* __res
                                                             const uint8_t* __restrict__ k_idx,
                                                             const float* __restrict__ k_scale,
                                                             const uint16_t* __restrict__ w, int H, dsa_seqs seqs,
-                                                            int64_t n_q, float* __restrict__ slab, int64_t ld) {
+                                                            int64_t n_q, float* __restrict__ slab, int64_t ld,
+                                                            int bf16_scores) {
   constexpr int D = 128;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t i = (int64_t)blockIdx.y * 4 + wave;
   if (i >= n_q) return;
   const int b = seq_of_row(seqs, i);
-  const int64_t p = seqs.q_pos0[b] + (i - seqs.q_start[b]);
+  const int64_t p = row_last(seqs, b, i);
   const int64_t s0 = (int64_t)blockIdx.x * kScoreKeysPerWave;
   if (s0 > p) return;
   const int64_t krow0 = seqs.k_start[b];
@@ -157,7 +160,9 @@ __global__ __launch_bounds__(256) void idx_score_fp8_kernel(const uint8_t* __res
     }
     part += __shfl_xor(part, 16);
     part += __shfl_xor(part, 32);
-    if (g == 0 && s <= p) slab[i * ld + s] = part * ks;
+    float sc = part * ks;
+    if (bf16_scores) sc = __uint_as_float(f32_to_bf16_bits(sc) << 16);
+    if (g == 0 && s <= p) slab[i * ld + s] = sc;
   }
 }
 
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(const float* _
   const int64_t i = blockIdx.x;
   if (i >= n_q) return;
   const int b = seq_of_row(seqs, i);
-  const int64_t n = seqs.q_pos0[b] + (i - seqs.q_start[b]) + 1;
+  const int64_t n = row_last(seqs, b, i) + 1;
   const float* row = slab + i * ld;
   int32_t* orow = idx_out + i * (int64_t)k;
   float* srow = score_out ? score_out + i * (int64_t)k : nullptr;
@@ -299,7 +304,10 @@ int64_t slab_ld(const dsa_seqs& s) {
   int64_t mx = 1;
   for (int b = 0; b < s.B; ++b) {
     const int64_t nq = s.q_start[b + 1] - s.q_start[b];
-    if (nq > 0) mx = mx > s.q_pos0[b] + nq ? mx : s.q_pos0[b] + nq;
+    if (nq <= 0) continue;
+    const int64_t t = s.q_pos0[b] + nq - 1;                 // the sequence's last query position
+    const int64_t n = s.block > 1 ? t / s.block : t + 1;    // keys it sees
+    mx = mx > n ? mx : n;
   }
   return (mx + 3) & ~int64_t(3);
 }
@@ -310,13 +318,14 @@ hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st
   const int64_t ld = slab_ld(a.seqs);
   dim3 grid((unsigned)((ld + kScoreKeysPerWave - 1) / kScoreKeysPerWave), (unsigned)((n_q + 3) / 4));
   const int HB = (a.H + 15) / 16;
+  const int bf16s = a.flags & DSA_TOPK_BF16_SCORES;
   if (a.qk_dtype == DSA_BF16) {
     const uint16_t* q = (const uint16_t*)a.q_idx;
     const uint16_t* kk = (const uint16_t*)a.k_idx;
 #define DSA_SCORE_BF16(HBv, Dv)                                                                        \
   if (HB == HBv && a.d == Dv) {                                                                      \
     hipLaunchKernelGGL((idx_score_bf16_kernel<HBv, Dv>), grid, dim3(256), 0, st, q, kk, a.w, a.H, a.seqs, \
-                       n_q, slab, ld);                                                               \
+                       n_q, slab, ld, bf16s);                                                               \
     return hipGetLastError();                                                                        \
   }
     DSA_SCORE_BF16(1, 64) DSA_SCORE_BF16(1, 128) DSA_SCORE_BF16(2, 64) DSA_SCORE_BF16(2, 128)
@@ -328,7 +337,7 @@ hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st
 #define DSA_SCORE_FP8(HBv)                                                                                 \
   if (HB == HBv && a.d == 128) {                                                                         \
     hipLaunchKernelGGL((idx_score_fp8_kernel<HBv>), grid, dim3(256), 0, st, q, a.q_scale, kk, a.k_scale, a.w, \
-                       a.H, a.seqs, n_q, slab, ld);                                                      \
+                       a.H, a.seqs, n_q, slab, ld, bf16s);                                                \
     return hipGetLastError();                                                                            \
   }
     DSA_SCORE_FP8(1) DSA_SCORE_FP8(2) DSA_SCORE_FP8(4)

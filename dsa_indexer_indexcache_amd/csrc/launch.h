@@ -18,6 +18,7 @@ struct IndexerArgs {
   dsa_seqs seqs;
   int32_t* idx_out;
   float* score_out;
+  int flags;  // DSA_TOPK_* (bf16-rounded scores)
 };
 
 struct AttnArgs {
@@ -53,6 +54,61 @@ hipError_t launch_quantize_fp8_rows(const uint16_t* x, int64_t rows, int cols, u
 constexpr int kOverlapMaxK = 16384;
 hipError_t launch_index_overlap(const int32_t* a, const int32_t* b, int64_t n_rows, int k, int32_t* counts,
                                 hipStream_t st);
+
+// proj.hip: indexer projections (query with RoPE; key with LayerNorm and RoPE; head weights
+// with the folded scales), d = 128; rope_dim in {0, 32, 64}; r and hidden multiples of 64.
+struct ProjectArgs {
+  const uint16_t* q_lat;
+  const uint16_t* h;
+  const uint16_t* wq;
+  const uint16_t* wk;
+  const float* gamma;
+  const float* beta;
+  const uint16_t* ww;
+  const int32_t* pos;
+  int64_t n;
+  int r, hidden, H, rope_dim;
+  float rope_base, eps;
+  uint16_t* q_idx;
+  uint16_t* k_idx;
+  uint16_t* w;
+};
+hipError_t launch_indexer_project(const ProjectArgs& a, hipStream_t st);
+hipError_t launch_cache_append(void* cache, int64_t cache_rows, const int64_t* dst_row, const void* rows,
+                               int64_t n_rows, int64_t row_bytes, hipStream_t st);
+
+// attn_stats.hip: attention statistics over a query's key sets (dense prefix / selected list):
+// captured mass and Recall@k against the dense top-k, the sparse-training indexer KL.
+struct StatArgs {
+  const uint16_t* q;
+  const uint16_t* latent;
+  const int32_t* idx;
+  int n_h, k;
+  float scale;
+  dsa_seqs seqs;
+};
+size_t attn_mass_ws(const StatArgs& a, bool recall);
+hipError_t launch_attention_mass(const StatArgs& a, float* mass_head, float* mass, float* recall, void* ws,
+                                 hipStream_t st);
+size_t indexer_kl_ws(const StatArgs& a);
+hipError_t launch_indexer_kl(const StatArgs& a, const float* scores, float weight, int accumulate, float* kl,
+                             float* loss, void* ws, hipStream_t st);
+
+// csa.hip: gated pooling of tokens n / m ... into compressed entries block0 .. n / m - 1;
+// c a multiple of 8; out [n / m - block0, c] in out_dtype (DSA_FP32 or DSA_BF16).
+struct CsaArgs {
+  const uint16_t* ca;
+  const uint16_t* cb;
+  const uint16_t* za;
+  const uint16_t* zb;
+  const float* ba;
+  const float* bb;
+  int64_t n, block0;
+  int c, m;
+  void* out;
+  int out_dtype;
+};
+hipError_t launch_csa_compress(const CsaArgs& a, hipStream_t st);
 
 // sparse_attn.hip
 int attn_splits(const AttnArgs& a);

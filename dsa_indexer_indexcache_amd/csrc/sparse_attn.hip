@@ -54,7 +54,7 @@ __global__ __launch_bounds__(512) void sparse_attn_kernel(const uint16_t* __rest
   const int split = blockIdx.x % splits;
   if (i >= n_q) return;
   const int b = seq_of_row(seqs, i);
-  const int64_t p = seqs.q_pos0[b] + (i - seqs.q_start[b]);
+  const int64_t p = row_last(seqs, b, i);
   const int64_t krow0 = seqs.k_start[b];
   const int c = lane & 15, g = lane >> 4;
   const int head0 = 16 * HG * wave;
@@ -255,6 +255,11 @@ constexpr int kTileIns = kTileBytes / 1024;       // 36 64-lane x 16-byte copies
 constexpr int kNBuf = 2;
 constexpr int kIdxMax = 2048;
 constexpr int kMaxWaves = 8;
+// Prefetch depths of the paired kernel's LDS reads (QK: 32-column steps; PV: column
+// groups).  Eight waves (two per SIMD, 256 registers each, q and O taking 200) only have
+// room for one step; four waves (one per SIMD) keep several reads in flight.
+template <int NW> constexpr int pf_k() { return NW >= 8 ? 1 : 3; }
+template <int NW> constexpr int pf_v() { return NW >= 8 ? 1 : 2; }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef v4i16 __attribute__((address_space(3))) lds_v4i16;
@@ -267,10 +272,6 @@ struct PairSmem {
   float bias[kIdxMax];          // 0 for a usable slot, -inf for a skipped one
 };
 
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
-// (lgkmcnt), not for outstanding global->LDS copies (vmcnt).  The "memory"
-// clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // LDS transpose read (4 x b16).  The gather into LDS is issued from asm, so the
 // compiler, which does not see it, schedules these reads with no wait for it.
@@ -282,23 +283,16 @@ __device__ __forceinline__ i32x4 pack_tr4(v4i16 lo, v4i16 hi) {
   return i32x4{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)(uint32_t)b, (int)(uint32_t)(b >> 32)};
 }
 
-// max over the four 16-lane rows of a wave (lanes c, c+16, c+32, c+48), all lanes get it
-__device__ __forceinline__ float max_over_rows(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
 
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
   return (uint32_t)((chunk >> 3) * (kBlk * 128) + row * 128 + 16 * ((chunk & 7) ^ (row & 7)));
 }
 
-// Workgroup b of the grid takes query row b % n_q, head group (b / n_q) % hgroups and
-// split b / (n_q hgroups) of the row's index list: consecutive workgroups take
-// consecutive rows, so with n_q = 8 every workgroup of a row is dispatched to the
-// same XCD (workgroups go round-robin over the 8 XCDs) and the head groups of a row
-// re-read its gathered latent rows from that XCD's L2.
+// Grid order: rows in blocks of 8; workgroup b takes row 8 rb + b % 8 of row block rb,
+// head group hg and split sp with b = ((sp * n_rb + rb) * hgroups + hg) * 8 + b % 8.
+// Workgroups go round-robin over the 8 XCDs, so all head groups (and, for one row
+// block, all splits) of a row run on one XCD close together in time and re-read the
+// row's gathered latent rows from that XCD's L2.
 template <int HG, int NW>
 __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_t* __restrict__ q,
                                                                    const uint16_t* __restrict__ latent,
@@ -313,14 +307,15 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int nwaves = NW;
   const int pair = wave >> 1, vh = wave & 1;
-  const uint32_t nq32 = (uint32_t)n_q;  // the grid is n_q * hgroups * splits < 2^32 workgroups
-  const int64_t i = blockIdx.x % nq32;
-  const uint32_t rest = blockIdx.x / nq32;
+  const uint32_t n_rb = (uint32_t)((n_q + 7) / 8);  // the grid is 8 n_rb hgroups splits < 2^32 workgroups
+  const uint32_t rest = blockIdx.x >> 3;
   const int hgi = (int)(rest % (uint32_t)hgroups);
-  const int split = (int)(rest / (uint32_t)hgroups);
-  if (split >= splits) return;
+  const uint32_t rs = rest / (uint32_t)hgroups;
+  const int64_t i = (int64_t)(rs % n_rb) * 8 + (blockIdx.x & 7);
+  const int split = (int)(rs / n_rb);
+  if (i >= n_q || split >= splits) return;
   const int b = seq_of_row(seqs, i);
-  const int64_t p = seqs.q_pos0[b] + (i - seqs.q_start[b]);
+  const int64_t p = row_last(seqs, b, i);
   const uint16_t* lat = latent + seqs.k_start[b] * kDqk;
   const int c = lane & 15, g = lane >> 4;
   const int head0 = 8 * HG * NW * hgi + 16 * HG * pair;
@@ -407,17 +402,32 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
     for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) st[hg][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // K fragment of step ks: column group ks, granule 4 vh + g of row 16 kt + c
+    // K fragment of step ks: column group ks, granule 4 vh + g of row 16 kt + c.  The
+    // fragments are read kPfK steps ahead of their MFMAs (scheduling barriers keep the
+    // order), so several LDS reads are in flight while the matrix core works.
+    constexpr int kPfK = pf_k<NW>();
     const uint8_t* kbase = tile + c * 128 + 16 * ((4 * vh + g) ^ (c & 7));
+    i32x4 kf[kPfK + 1][2];
+#pragma unroll
+    for (int j = 0; j < kPfK; ++j)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) kf[j][kt] = *reinterpret_cast<const i32x4*>(kbase + j * (kBlk * 128) + kt * 2048);
 #pragma unroll
     for (int ks = 0; ks < 9; ++ks) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (ks + kPfK < 9) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const i32x4 kf = *reinterpret_cast<const i32x4*>(kbase + ks * (kBlk * 128) + kt * 2048);
-#pragma unroll
-        for (int hg = 0; hg < HG; ++hg) st[hg][kt] = mfma_bf16_16x16x32(kf, qf[hg][ks], st[hg][kt]);
+        for (int kt = 0; kt < 2; ++kt)
+          kf[(ks + kPfK) % (kPfK + 1)][kt] =
+              *reinterpret_cast<const i32x4*>(kbase + (ks + kPfK) * (kBlk * 128) + kt * 2048);
       }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int hg = 0; hg < HG; ++hg)
+          st[hg][kt] = mfma_bf16_16x16x32(kf[ks % (kPfK + 1)][kt], qf[hg][ks], st[hg][kt]);
     }
+    __builtin_amdgcn_sched_barrier(0);
     // ---- exchange partial scores with the partner wave
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg)
@@ -485,18 +495,33 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
     const int r0 = 4 * g + tj;
     const uint8_t* vb0 = tile + r0 * 128 + 16 * ((2 * vh + (ta >> 1)) ^ (r0 & 7)) + 8 * (ta & 1);
     const uint8_t* vb1 = tile + r0 * 128 + 16 * ((4 + 2 * vh + (ta >> 1)) ^ (r0 & 7)) + 8 * (ta & 1);
-    // tiles vt (even: base 0) and vt + 1 (odd: base 1) share column group vt / 2
+    // tiles vt (even: base 0) and vt + 1 (odd: base 1) share column group vt / 2; the
+    // transpose reads run kPfV column groups ahead of their MFMAs
+    constexpr int kPfV = pf_v<NW>();
+    v4i16 vr[kPfV + 1][4];
+    auto vread = [&](int it, v4i16 (&d)[4]) {
+      const int cgo = it * (kBlk * 128);
+      d[0] = tr16(vb0 + cgo);
+      d[1] = tr16(vb0 + cgo + 2048);
+      d[2] = tr16(vb1 + cgo);
+      d[3] = tr16(vb1 + cgo + 2048);
+    };
 #pragma unroll
-    for (int vt = 0; vt < 16; vt += 2) {
-      const int cgo = (vt >> 1) * (kBlk * 128);
-      const i32x4 vfe = pack_tr4(tr16(vb0 + cgo), tr16(vb0 + cgo + 2048));
-      const i32x4 vfo = pack_tr4(tr16(vb1 + cgo), tr16(vb1 + cgo + 2048));
+    for (int j = 0; j < kPfV; ++j) vread(j, vr[j]);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + kPfV < 8) vread(it + kPfV, vr[(it + kPfV) % (kPfV + 1)]);
+      const v4i16 (&cur)[4] = vr[it % (kPfV + 1)];
+      const i32x4 vfe = pack_tr4(cur[0], cur[1]);
+      const i32x4 vfo = pack_tr4(cur[2], cur[3]);
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg) {
-        o[hg][vt] = mfma_bf16_16x16x32(pf[hg], vfe, o[hg][vt]);
-        o[hg][vt + 1] = mfma_bf16_16x16x32(pf[hg], vfo, o[hg][vt + 1]);
+        o[hg][2 * it] = mfma_bf16_16x16x32(pf[hg], vfe, o[hg][2 * it]);
+        o[hg][2 * it + 1] = mfma_bf16_16x16x32(pf[hg], vfo, o[hg][2 * it + 1]);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- finish
@@ -622,7 +647,7 @@ AttnPlan attn_plan(const AttnArgs& a) {
     pl.hg = 1;
     pl.nw = a.n_h / 16;
   }
-  if (n_q >= 512 || nblk <= 1) return pl;
+  if (n_q >= 512 || nblk <= 1) return pl;  // many rows: one workgroup per row with every head
   if (pl.paired) {
     pl.hg = 1;       // a pair per 16 heads, two pairs per workgroup
     pl.nw = 4;
@@ -659,7 +684,9 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
     part_o = (float*)ws;
     part_ml = part_o + (size_t)n_q * splits * a.n_h * kDv;
   }
-  dim3 grid((unsigned)(n_q * pl.hgroups * splits));
+  // the paired kernel takes rows in blocks of 8 (see its grid order), the other one row each
+  const int64_t rows_grid = pl.paired ? (n_q + 7) / 8 * 8 : n_q;
+  dim3 grid((unsigned)(rows_grid * pl.hgroups * splits));
   float* of = splits == 1 ? out_f32 : nullptr;
   uint16_t* ob = splits == 1 ? out_bf16 : nullptr;
   if (pl.paired) {

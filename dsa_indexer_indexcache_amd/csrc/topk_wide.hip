@@ -59,7 +59,7 @@ __device__ __forceinline__ uint64_t wkey64(uint32_t key, uint32_t pos) {
 
 __device__ __forceinline__ int64_t row_len(const dsa_seqs& s, int64_t i) {
   const int b = seq_of_row(s, i);
-  return s.q_pos0[b] + (i - s.q_start[b]) + 1;
+  return row_last(s, b, i) + 1;
 }
 
 __global__ __launch_bounds__(kWThreads) void wsel_zero_kernel(WideWs w) {

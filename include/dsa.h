@@ -64,10 +64,14 @@ typedef enum {
  *   prefill chunk: B = 1, q_pos0[0] = position of the chunk's first query;
  *   decode step:   q_start = {0,1,..,B}, q_pos0[b] = len_b - 1 (the new token
  *                  is already in the caches).
+ * block (0 or 1: token keys): the key rows are compressed blocks of `block` tokens
+ * (the compressed-block selection of [IDX] §5.2): a query at token position t sees
+ * blocks s < floor(t / block), i.e. up to s = floor(t / block) - 1 (none while
+ * t < block), and floor(t_last / block) <= k_start[b+1] - k_start[b] must hold.
  */
 typedef struct {
   int32_t B;
-  int32_t reserved;
+  int32_t block;
   int64_t q_start[DSA_MAX_B + 1];
   int64_t k_start[DSA_MAX_B + 1];
   int64_t q_pos0[DSA_MAX_B];
@@ -99,6 +103,17 @@ typedef struct {
 int dsa_indexer_topk(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
                      const uint16_t* w, int qk_dtype, int H, int d, int k, const dsa_seqs* seqs /* host */,
                      int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_indexer_topk with selection flags.  DSA_TOPK_BF16_SCORES: every score is rounded
+ * to bf16 (nearest even) before the ranking, the lower-precision selector of [IDX] §5.4
+ * (which quantises index scores from fp32 to bf16); more scores tie, ties still go to the
+ * lower position, and score_out holds the rounded values.  flags == 0 is dsa_indexer_topk.
+ */
+#define DSA_TOPK_BF16_SCORES 1
+int dsa_indexer_topk_ex(const void* q_idx, const float* q_scale, const void* k_idx, const float* k_scale,
+                        const uint16_t* w, int qk_dtype, int H, int d, int k, const dsa_seqs* seqs /* host */,
+                        int32_t* idx_out, float* score_out, void* ws, size_t ws_bytes, int flags, void* stream);
 
 /* Workspace bytes dsa_indexer_topk needs for this shape: 0 for one-sequence
  * prefill with at least 256 query rows, k <= 2048 and d in {64,128} (scores never
@@ -148,7 +163,7 @@ typedef struct {
   float scale;              /* softmax scale (1/sqrt(d_qk) for MLA)     */
   int32_t qk_dtype;         /* dsa_dtype of q_idx/k_idx                 */
   int32_t out_dtype;        /* dsa_dtype of out (DSA_FP32 or DSA_BF16)  */
-  int32_t reserved;
+  int32_t flags;            /* DSA_TOPK_* flags of the F layers' selection */
   int64_t q_chunk;          /* query rows per chunk (>= 1)               */
   int64_t index_rows;       /* rows of index_cache / score_cache         */
   int64_t out_rows;         /* rows of every layer's out buffer           */
@@ -252,6 +267,101 @@ int dsa_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t n_rows
  * rows < 0 or a null pointer gives DSA_ERR_INVALID_ARG.
  */
 int dsa_quantize_fp8_rows(const uint16_t* x, int64_t rows, int cols, uint8_t* codes, float* scales, void* stream);
+
+/*
+ * Index-quality metrics of one query row ([IDX] §8 items 1 and 2), from the main
+ * attention's dense weights alpha[t, h, s] = softmax over s <= t of scale q[t,h].c[s]
+ * (the dense attention of [IDX] §1; keys = all d_qk latent columns):
+ *   mass_head[i, h] = CapturedMass@k of head h = sum over s in S_i of alpha[t, h, s]
+ *   mass[i]         = the same for the head-aggregated distribution p_t (heads summed,
+ *                     then L1-normalised: the mean of mass_head over h); MissedMass = 1 - mass
+ *   recall[i]       = Recall@k = |S^oracle_i ∩ S_i| / |S^oracle_i|, S^oracle_i the min(k, t+1)
+ *                     positions of largest p_t[s] (ties to the lower position)
+ * S_i are the valid entries (0 <= s <= t) of idx[i, :] (the model's selection).
+ *   q [n_q, n_h, d_qk] bf16, latent [n_k, d_qk] bf16, idx [n_q, k] int32 (device);
+ *   mass [n_q] fp32 (required), mass_head [n_q, n_h] fp32 and recall [n_q] fp32 (optional).
+ * Scores and sums in fp32.  Supported: n_h in {16,32,64,128}, d_qk == 576, k <= 2048.
+ * The dense pass costs O(t n_h d_qk) per row: a metric for short contexts.  The workspace
+ * (dsa_attention_mass_ws) holds two per-head log-sum-exp tables and, with recall, an fp32
+ * row of p_t per query (n_q x longest prefix).
+ */
+size_t dsa_attention_mass_ws(int n_h, int k, const dsa_seqs* seqs /* host */, int want_recall);
+int dsa_attention_mass(const uint16_t* q, const uint16_t* latent, const int32_t* idx, int n_h, int d_qk, int k,
+                       float scale, const dsa_seqs* seqs /* host */, float* mass_head, float* mass, float* recall,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse-training indexer loss ([IDX] §4.2: D_KL(p_{t,S_t} || Softmax(I_{t,S_t})), p the
+ * main attention's weights over S_t summed over heads and L1-normalised; [IC] §3.1: an F
+ * layer serving m S layers averages the KL against each served layer's p):
+ *   kl[i] = (accumulate ? kl[i] : 0) + weight * D_KL(p_i || softmax(scores[i, valid slots]))
+ * with the attention over the valid slots of idx[i, :] (this layer's q and latent) and
+ * scores[i, j] the indexer score of slot j (as dsa_indexer_topk's score_out).  The
+ * multi-layer loss: call once per served layer with weight 1/(m+1), accumulate = 0 for
+ * the first.  loss (optional, device fp32 scalar) receives sum_i kl[i] (fixed-order sum).
+ * A row with no valid slot contributes 0.  Supported as dsa_attention_mass.
+ */
+size_t dsa_indexer_kl_ws(int n_h, int k, const dsa_seqs* seqs /* host */);
+int dsa_indexer_kl(const uint16_t* q, const uint16_t* latent, const int32_t* idx, const float* scores, int n_h,
+                   int d_qk, int k, float scale, const dsa_seqs* seqs /* host */, float weight, int accumulate,
+                   float* kl, float* loss, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- upstream of the indexer */
+/*
+ * The indexer's inputs from the token's low-rank query latent and hidden state
+ * ([IDX] §6.4, the GLM indexer: a query projection split into H heads of d, a key
+ * projection followed by a LayerNorm over d, head weights from the hidden state times
+ * H^-1/2, a score scaled by d^-1/2, rotary encoding of the query/key rotary part):
+ *   q_idx[t, j, :] = RoPE(q_lat[t] . wq[j d .. j d + d, :]^T, pos[t])
+ *   k_idx[t, :]    = RoPE(LayerNorm(h[t] . wk^T) * ln_weight + ln_bias, pos[t])
+ *   w[t, j]        = (h[t] . ww[j, :]^T) * H^-1/2 * d^-1/2
+ * RoPE rotates dimension pairs (i, i + rope_dim/2), i < rope_dim/2, by the angle
+ * pos * rope_base^(-2i/rope_dim) (angles in fp64); dimensions from rope_dim on pass
+ * through.  The score's positive d^-1/2 is folded into w (it commutes with the ReLU),
+ * so these outputs feed dsa_indexer_topk unchanged.  LayerNorm: population variance, eps.
+ *   q_lat [n, r] bf16; h [n, hidden] bf16; wq [H d, r], wk [d, hidden], ww [H, hidden]
+ *   bf16 (nn.Linear layout: [out, in]); ln_weight, ln_bias [d] fp32; pos [n] int32;
+ *   outputs q_idx [n, H, d], k_idx [n, d], w [n, H] bf16 (fp32 accumulation, rounded once).
+ * Supported: d == 128, 1 <= H <= 128, rope_dim in {0, 32, 64}, r and hidden positive
+ * multiples of 64 (else DSA_ERR_UNSUPPORTED).  n == 0 is a no-op.  For the fp8 indexer,
+ * dsa_quantize_fp8_rows turns q_idx / k_idx into codes and scales.
+ */
+int dsa_indexer_project(const uint16_t* q_lat, const uint16_t* h, const uint16_t* wq, const uint16_t* wk,
+                        const float* ln_weight, const float* ln_bias, const uint16_t* ww, const int32_t* pos, int64_t n,
+                        int r, int hidden, int H, int d, int rope_dim, float rope_base, float eps, uint16_t* q_idx,
+                        uint16_t* k_idx, uint16_t* w, void* stream);
+
+/*
+ * KV compression of compressed sparse attention ([IDX] §5.1, DeepSeek-V4 CSA): every m
+ * tokens become one entry by a gated pooling over an overlapping window of 2m rows.
+ * Entry i, for each feature column j separately, weighs the a-half rows m i .. m i + m - 1
+ * and the b-half rows m (i-1) .. m i - 1 by one softmax over the 2m gate logits
+ *   za[m i + r, j] + ba[r, j]   and   zb[m (i-1) + r, j] + bb[r, j]   (r < m)
+ * and writes the weighted sum of ca[m i + r, j] and cb[m (i-1) + r, j].  Entry 0 has no
+ * b-half (its window would start before token 0) and pools the a-half alone.  Only
+ * complete groups of m tokens form entries: entries block0 .. n / m - 1 are computed,
+ * entry block0 + e written to row e of out (a decode step that completes a group passes
+ * block0 = n / m - 1 and all n tokens' rows).
+ *   ca, cb, za, zb [n, c] bf16 (the projections C^a, C^b, Z^a, Z^b of the tokens);
+ *   ba, bb [m, c] fp32 (positional gate biases); out [n / m - block0, c] in out_dtype
+ *   (DSA_FP32 or DSA_BF16, rounded to nearest even once).  fp32 arithmetic.
+ * Supported: c a positive multiple of 8, 1 <= m <= 4096.  n / m <= block0 is a no-op.
+ * The compressed rows are keys of dsa_indexer_topk with seqs->block = m.
+ */
+int dsa_csa_compress(const uint16_t* ca, const uint16_t* cb, const uint16_t* za, const uint16_t* zb,
+                     const float* ba, const float* bb, int64_t n, int c, int m, int64_t block0, void* out,
+                     int out_dtype, void* stream);
+
+/*
+ * Decode-time cache write ([IDX] §4: every new token is written into the caches before
+ * the read of the same step): row b of `rows` (row_bytes bytes) is copied to row
+ * dst_row[b] of `cache` (cache_rows rows of row_bytes).  A packed per-sequence cache with
+ * sequence b at k_start[b] and len_b tokens takes dst_row[b] = k_start[b] + len_b.
+ *   cache (device, written); dst_row [n_rows] int64 (device); rows [n_rows, row_bytes] (device)
+ * A destination outside [0, cache_rows) is skipped for that row.  n_rows == 0 is a no-op.
+ */
+int dsa_cache_append(void* cache, int64_t cache_rows, const int64_t* dst_row, const void* rows, int64_t n_rows,
+                     int64_t row_bytes, void* stream);
 
 /* ---------------------------------------------------------------- misc */
 const char* dsa_status_string(int status); /* static string                         */

@@ -227,6 +227,16 @@ def decode_layer(layer: int, lens: Sequence[int], device: str = "cpu", wid: int 
                       qk_dtype=w.qk_dtype, device=device)
 
 
+def csa_inputs(n: int, c: int, m: int, seed: int = 0):
+    """Token-level inputs of the KV compression of compressed sparse attention: values C^a, C^b
+    and gate logits Z^a, Z^b [n, c] bf16 N(0,1); gate biases B^a, B^b [m, c] fp32 N(0, 1/4)."""
+    g = np.random.default_rng([0xC5A, n, c, m, seed])
+    vals = [to_bf16(torch.from_numpy(g.standard_normal((n, c), dtype=np.float32))) for _ in range(4)]
+    biases = [torch.from_numpy((0.5 * g.standard_normal((m, c))).astype(np.float32)) for _ in range(2)]
+    ca, cb, za, zb = vals
+    return ca, cb, za, zb, biases[0], biases[1]
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """Raw storage bits of a bf16 / fp8 tensor as a NumPy unsigned array (host copy)."""
     t = t.detach().cpu().contiguous()

@@ -15,6 +15,7 @@ import numpy as np
 import torch
 
 import oracle
+from oracle import csa as ocsa
 import synth
 
 SCORE_REL = 1e-3
@@ -31,11 +32,15 @@ def sample_rows(n_q: int, k: int, n: int = 32, seed: int = 0, extra=()) -> list:
 
 
 def row_geometry(seqs, i: int):
-    """(position p, first key row k0) of packed query row i."""
+    """(last visible key p, first key row k0) of packed query row i: its position t over
+    token keys; over compressed blocks of m = seqs.block tokens, t // m - 1 (-1: none)."""
     b = 0
     while b + 1 < seqs.B and i >= seqs.q_start[b + 1]:
         b += 1
-    return int(seqs.q_pos0[b] + (i - seqs.q_start[b])), int(seqs.k_start[b])
+    t = int(seqs.q_pos0[b] + (i - seqs.q_start[b]))
+    if seqs.block > 1:
+        t = ocsa.visible_blocks(t, int(seqs.block)) - 1
+    return t, int(seqs.k_start[b])
 
 
 def _deq(t: torch.Tensor, scale) -> np.ndarray:
@@ -98,6 +103,9 @@ def check_indexer(view: OracleView, seqs, rows, k: int, idx_gpu: torch.Tensor, s
         ro, kth, m = oracle.topk_row(I, k)
         check_valid_row(ig[n], p, k)
         got = ig[n][:m]
+        if m == 0:
+            recalls.append(1.0)
+            continue
         if exact:
             assert np.array_equal(got, ro[:m]), "row %d: index set differs" % i
             if sg is not None:
@@ -140,3 +148,46 @@ def check_attention(view: OracleView, seqs, rows, idx_gpu: torch.Tensor, out_gpu
         worst = max(worst, err)
         assert err <= ATTN_ATOL, "row %d: attention max abs error %g > %g" % (i, err, ATTN_ATOL)
     return worst
+
+
+def check_indexer_bf16(view: OracleView, seqs, rows, k: int, idx_gpu: torch.Tensor, sc_gpu: torch.Tensor):
+    """Checks a bf16-score selection (scores rounded to bf16 before the ranking).
+
+    The oracle rounds its fp64 score through fp32 to bf16 (nearest even); the GPU rounds
+    its fp32 sum, which lies within the fp32 tolerance of the fp64 score, so a score whose
+    fp64 value sits within that tolerance of a rounding midpoint may round either way.
+    Rules per row: every returned score is a bf16 value and equals the oracle's rounded
+    score or, for such a score, its neighbour; the set equals the oracle's selection
+    (rounded scores descending, ties to the lower position) except for keys whose rounded
+    score is within one bf16 step of the k-th rounded score; mean recall >= 0.995."""
+    rows = list(rows)
+    qv, wv = view.q_idx_rows(rows), view.w_rows(rows)
+    keys = view.keys()
+    r = torch.as_tensor(rows, device=idx_gpu.device)
+    ig = idx_gpu[r].cpu().numpy()
+    sg = sc_gpu[r].cpu().numpy()
+    recalls = []
+    for n, i in enumerate(rows):
+        p, k0 = row_geometry(seqs, i)
+        I = oracle.indexer_row(qv[n], wv[n], keys[k0:k0 + p + 1])
+        Ib = ocsa.round_bf16(I)
+        ro, kth, m = oracle.topk_row(Ib, k)
+        check_valid_row(ig[n], p, k)
+        got = ig[n][:m]
+        if m == 0:
+            recalls.append(1.0)
+            continue
+        tol = oracle.tolerance_row(I, SCORE_REL)
+        s = sg[n][:m]
+        assert np.all(s.view(np.uint32) & 0xFFFF == 0), "row %d: scores are not bf16 values" % i
+        lo, hi = ocsa.round_bf16(I[got] - tol), ocsa.round_bf16(I[got] + tol)
+        assert np.all((s >= lo) & (s <= hi)), "row %d: a bf16 score is off its rounding range" % i
+        step = 2.0 ** (np.floor(np.log2(max(abs(kth), 1e-30))) - 7)
+        a, b = set(got.tolist()), set(ro[:m].tolist())
+        recalls.append(len(a & b) / m)
+        for x in a ^ b:
+            assert abs(Ib[x] - kth) <= step + tol, "row %d: mismatch at %d is %g from the k-th score" % (
+                i, x, abs(Ib[x] - kth))
+    mean = float(np.mean(recalls)) if recalls else 1.0
+    assert mean >= 0.995, "mean recall %.5f" % mean
+    return {"rows": len(rows), "recall_mean": mean}

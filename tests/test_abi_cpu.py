@@ -220,3 +220,66 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
     assert b"scratch" in L.dsa_last_error()
     assert L.indexcache_forward_noalloc(b"SF", layers, ctypes.byref(shape), ctypes.byref(seqs), None, None, None,
                                         None) == -3
+
+
+def test_indexer_project_validation():
+    """Argument checks of dsa_indexer_project run before any launch."""
+    L = dsa.lib()
+    z = [None] * 8
+    ok = dict(n=4, r=128, hidden=256, H=64, d=128, rope=64)
+
+    def call(n=4, r=128, hidden=256, H=64, d=128, rope=64, base=10000.0, eps=1e-5):
+        return L.dsa_indexer_project(*z, n, r, hidden, H, d, rope, base, eps, None, None, None, None)
+    assert call(n=0) == 0                        # no tokens: a no-op
+    assert call(n=-1) == -1
+    assert call(d=64) == -4                      # only d = 128 is compiled
+    assert call(H=0) == -4 and call(H=129) == -4
+    assert call(rope=48) == -4
+    assert call(r=100) == -4 and call(hidden=32) == -4
+    assert call(base=1.0) == -1 and call(eps=-1.0) == -1
+    assert call() == -1                          # null pointers
+    assert ok
+
+
+def test_cache_append_validation():
+    L = dsa.lib()
+    assert L.dsa_cache_append(None, 10, None, None, 0, 16, None) == 0      # no rows: a no-op
+    assert L.dsa_cache_append(None, 10, None, None, -1, 16, None) == -1
+    assert L.dsa_cache_append(None, 10, None, None, 2, 0, None) == -1
+    assert L.dsa_cache_append(None, 10, None, None, 2, 16, None) == -1     # null pointers
+    assert L.dsa_cache_append(None, 10, None, None, 2 ** 31, 16, None) == -4
+
+
+def test_compressed_block_table_validation():
+    """seqs->block: a negative ratio is rejected; with block m the last query t needs t // m keys."""
+    ok = dsa.Seqs.compressed(100, 4)                                 # t = 99 needs 24 blocks, has 25
+    assert ok.block == 4 and ok.n_k == 25
+    short = dsa.Seqs.compressed(100, 4, n_k=23)                      # t = 99 needs 24
+    assert _topk(seqs=short) == -1
+    assert b"needs 24 keys" in dsa.lib().dsa_last_error()
+    neg = dsa.Seqs.compressed(100, 4)
+    neg.block = -2
+    assert _topk(seqs=neg) == -1
+
+
+def test_topk_ex_rejects_unknown_flags():
+    L = dsa.lib()
+    s = dsa.Seqs.prefill(100)
+    rc = L.dsa_indexer_topk_ex(FAKE, None, FAKE, None, FAKE, 0, 64, 128, 2048, ctypes.byref(s), FAKE, None, FAKE,
+                               1 << 40, 6, None)
+    assert rc == -1 and b"flags" in L.dsa_last_error()
+
+
+def test_csa_compress_validation():
+    L = dsa.lib()
+    f = lambda **kw: L.dsa_csa_compress(*[kw.get(n, FAKE) for n in ("ca", "cb", "za", "zb", "ba", "bb")],
+                                        kw.get("n", 64), kw.get("c", 128), kw.get("m", 4), kw.get("b0", 0),
+                                        kw.get("out", FAKE), kw.get("odt", 0), None)
+    assert f(m=0) == -4 and f(m=5000) == -4
+    assert f(c=100) == -4 and f(c=0) == -4
+    assert f(n=-1) == -1 and f(b0=-1) == -1
+    assert f(odt=1) == -1                                            # fp8 output is not offered
+    assert f(n=3, ca=None) == 0                                      # fewer than m tokens: no entry, a no-op
+    assert f(n=64, b0=16, ca=None) == 0                              # block0 past the last entry: a no-op
+    assert f(ca=None) == -1
+    assert f(ca=FAKE + 8) == -5
