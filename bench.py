@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=4,
                     help="synthetic workload id (4 = L=200K FSSS fp8; 3 = decode B=8 over 47 layers)")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement after the prefill line")
+    ap.add_argument("--no-widened", action="store_true",
+                    help="skip the projection / statistics / compressed-attention measurements")
+    ap.add_argument("--widened-only", action="store_true", help="only print the widened rows' measurements")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the L=32768 single-layer and L=65536 FSSSFSSS measurements after the headline")
     ap.add_argument("--L", type=int, default=None, help="override the context length (development only)")
@@ -219,6 +222,140 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_bytes_per_launch": n, "launches": 2}), flush=True)
 
 
+def _time_ms(fn, reps: int = 10) -> float:
+    """Mean device time of fn() over reps back-to-back calls on torch's current stream
+    (the binding enqueues every library call on it)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_widened_rows() -> dict:
+    """The entry points beside the hot path, each at a shape of the pages' setting:
+    indexer projections of one 8192-token chunk, the decode cache append, the attention
+    statistics and indexer KL of one chunk, and compressed sparse attention (m = 4): the
+    KV compression of 65,536 tokens and the compressed-block selection in prefill and decode."""
+    import torch
+
+    import dsa_indexer_indexcache_amd as dsa
+    import synth
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    rnd = lambda *shape, div=1.0: (torch.randn(*shape, generator=g, device=dev) / div).to(torch.bfloat16)
+    out = {}
+
+    # indexer projections: q_lat [n, 1536] -> q [n, 64, 128] (RoPE 64), h [n, 7168] -> key
+    # (LayerNorm, RoPE) and head weights; 2 n (r H d + hidden d + hidden H) flops
+    n, r, hid, H, d = 8192, 1536, 7168, 64, 128
+    q_lat, h = rnd(n, r), rnd(n, hid)
+    wq, wk, ww = rnd(H * d, r, div=r ** 0.5), rnd(d, hid, div=hid ** 0.5), rnd(H, hid, div=hid ** 0.5)
+    gam, bet = torch.ones(d, device=dev), torch.zeros(d, device=dev)
+    pos = torch.arange(n, dtype=torch.int32, device=dev)
+    qo = torch.empty((n, H, d), dtype=torch.bfloat16, device=dev)
+    ko = torch.empty((n, d), dtype=torch.bfloat16, device=dev)
+    wo = torch.empty((n, H), dtype=torch.bfloat16, device=dev)
+    ms = _time_ms(lambda: dsa.indexer_project(q_lat, h, wq, wk, gam, bet, ww, pos, H, rope_dim=64, q_idx=qo,
+                                              k_idx=ko, w=wo))
+    fl = 2.0 * n * (r * H * d + hid * d + hid * H)
+    out["indexer_project"] = {"n": n, "r": r, "hidden": hid, "H": H, "d": d, "rope_dim": 64, "ms": ms,
+                              "tflops": fl / (ms * 1e-3) / 1e12, "frac_bf16_peak": fl / (ms * 1e-3) / PEAK["bf16"]}
+    del q_lat, h, wq, wk, ww, qo, ko, wo
+
+    # decode cache append: 8 new 1152-byte latent rows into a 1.6M-row packed cache
+    cache = torch.empty((1_600_000, 576), dtype=torch.bfloat16, device=dev)
+    rows = rnd(8, 576)
+    dst = torch.arange(8, dtype=torch.int64, device=dev) * 200_000 + 199_000
+    ms = _time_ms(lambda: dsa.cache_append(cache, dst, rows), reps=50)
+    out["cache_append"] = {"rows": 8, "row_bytes": 1152, "us_per_launch": 1e3 * ms}
+    del cache
+
+    # attention statistics of the last 256 rows of a 32,768-token prefix (128 heads) and the
+    # indexer KL of one 8192-row chunk over its selected lists (k = 2048).  A q.c product is
+    # 2 x 576 flops per (row, head, key).  Captured mass + Recall@k: the dense log-sum-exp
+    # needs one pass over the prefix and the head-aggregated weights p (for the dense top-k)
+    # a second one, as p needs the finished log-sum-exp; plus one pass over S_t.  The KL:
+    # a log-sum-exp pass and a weight pass over S_t.
+    L, k = 32768, 2048
+    li = synth.make_layer(L, L, 64, 128, 128, wid=1, layer=0, device=dev)
+    rows_m = 256
+    sq = dsa.Seqs.prefill(rows_m, n_k=L, q_pos0=L - rows_m)
+    idx_m, _ = dsa.indexer_topk(li.q_idx[-rows_m:], li.k_idx, li.w[-rows_m:], k, sq)
+    ms = _time_ms(lambda: dsa.attention_mass(li.q[-rows_m:], li.latent, idx_m, sq), reps=3)
+    pairs = float(np.arange(L - rows_m + 1, L + 1).sum())
+    fl = 2.0 * 576 * 128 * (2 * pairs + rows_m * k)
+    out["attention_mass_recall"] = {"rows": rows_m, "prefix": L, "n_h": 128, "k": k, "ms": ms,
+                                    "rows_per_s": rows_m / (ms * 1e-3), "tflops": fl / (ms * 1e-3) / 1e12,
+                                    "frac_bf16_peak": fl / (ms * 1e-3) / PEAK["bf16"]}
+    c0 = L - 8192
+    sk = dsa.Seqs.prefill(8192, n_k=L, q_pos0=c0)
+    idx_k, sc_k = dsa.indexer_topk(li.q_idx[c0:], li.k_idx, li.w[c0:], k, sk, want_scores=True)
+    ms = _time_ms(lambda: dsa.indexer_kl(li.q[c0:], li.latent, idx_k, sc_k, sk), reps=3)
+    fl = 2 * 2.0 * 576 * 128 * 8192 * k
+    out["indexer_kl"] = {"rows": 8192, "k": k, "n_h": 128, "ms": ms, "tflops": fl / (ms * 1e-3) / 1e12,
+                         "frac_bf16_peak": fl / (ms * 1e-3) / PEAK["bf16"]}
+    del li, idx_m, idx_k, sc_k
+
+    # CSA KV compression of 65,536 tokens (m = 4) for the 576-wide latent and the 128-wide
+    # indexer key: reads C^a, Z^a of every token and C^b, Z^b of all but the last group
+    # (2 B each), writes one bf16 entry per group
+    m, n = 4, 65536
+    csa = {}
+    for c in (576, 128):
+        ca, cb, za, zb = rnd(n, c), rnd(n, c), rnd(n, c), rnd(n, c)
+        ba, bb = torch.zeros((m, c), device=dev), torch.zeros((m, c), device=dev)
+        o = torch.empty((n // m, c), dtype=torch.bfloat16, device=dev)
+        ms = _time_ms(lambda: dsa.csa_compress(ca, cb, za, zb, ba, bb, m, out=o), reps=20)
+        nbytes = 2.0 * c * (2 * n + 2 * (n - m)) + 2.0 * c * (n // m)
+        csa["compress_c%d" % c] = {"tokens": n, "m": m, "us": 1e3 * ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                                   "hbm_frac": nbytes / (ms * 1e-3) / PEAK["hbm"]}
+        del ca, cb, za, zb, o
+
+    # compressed-block selection, prefill: 65,536 query tokens over 16,384 blocks (fp8,
+    # H = 64, d = 128, k = 2048); flops 2 H d per visible (query, block) pair
+    li = synth.make_layer(n, n // m, 64, 128, 16, wid=4, layer=0, qk_dtype="fp8", device=dev, with_attention=False)
+    sc = dsa.Seqs.compressed(n, m)
+    for bf16s in (False, True):
+        ms = _time_ms(lambda: dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 2048, sc, q_scale=li.q_scale,
+                                               k_scale=li.k_scale, bf16_scores=bf16s), reps=3)
+        pairs = float((np.arange(n) // m).sum())
+        fl = 2.0 * 64 * 128 * pairs
+        csa["select_prefill_%s" % ("bf16_scores" if bf16s else "fp32_scores")] = {
+            "queries": n, "blocks": n // m, "k": 2048, "ms": ms, "queries_per_s": n / (ms * 1e-3),
+            "tflops": fl / (ms * 1e-3) / 1e12, "frac_fp8_peak": fl / (ms * 1e-3) / PEAK["fp8"]}
+    del li
+
+    # compressed-block selection, decode: B = 8 single queries over 150K-200K-token
+    # contexts (37K-50K blocks each), and the recall of the fp32 selection by the bf16 one
+    lens = synth.decode_lengths()
+    nb = [int(x) // m for x in lens]
+    li = synth.make_layer(8, int(np.sum(nb)), 64, 128, 16, wid=3, layer=0, qk_dtype="bf16", device=dev,
+                          with_attention=False)
+    sd = dsa.Seqs.varlen([1] * 8, nb, [int(x) - 1 for x in lens], block=m)
+    i32 = torch.empty((8, 2048), dtype=torch.int32, device=dev)
+    i16 = torch.empty_like(i32)
+    ms32 = _time_ms(lambda: dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 2048, sd, idx_out=i32), reps=20)
+    ms16 = _time_ms(lambda: dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 2048, sd, idx_out=i16, bf16_scores=True),
+                    reps=20)
+    cnt = dsa.index_overlap(i16, i32).float()
+    rec = float((cnt / 2048).mean())
+    kbytes = 2.0 * 128 * float(np.sum(nb))
+    csa["select_decode_B8"] = {"blocks": nb, "us_fp32_scores": 1e3 * ms32, "us_bf16_scores": 1e3 * ms16,
+                               "key_hbm_frac_fp32": kbytes / (ms32 * 1e-3) / PEAK["hbm"],
+                               "recall_of_fp32_selection_by_bf16": rec}
+    out["csa"] = csa
+    del li
+    torch.cuda.synchronize()
+    return out
+
+
 def run_decode(steps: int, warmup: int, hip, all_f: bool = True) -> dict:
     """Decode step of the 47-layer stack: 8 sequences, one new query each, context
     lengths drawn from [150000, 200000]; every layer's caches resident in HBM."""
@@ -287,6 +424,32 @@ def run_decode(steps: int, warmup: int, hip, all_f: bool = True) -> dict:
            "sparse_attn_hbm_frac": attn_bytes / (attn_ms * 1e-3) / PEAK["hbm"],
            "indexer_bytes_per_F_layer": idx_bytes, "attn_bytes_per_layer": attn_bytes,
            "indexer_work_saved": 1.0 - n_f / len(roles)}
+    # the same step captured once as a HIP graph (no host work or launch gaps between the
+    # 47 layers' kernels) and replayed; the library records no events inside the capture
+    step(roles)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(roles)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step(roles)
+    torch.cuda.synchronize()
+    gw = []
+    for _ in range(max(steps, 5)):
+        flush_infinity_cache(flush)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        graph.replay()
+        torch.cuda.synchronize()
+        gw.append(1e3 * (time.perf_counter() - t0))
+    kern_ms = (idx_ms * n_f + attn_ms * len(roles))
+    res.update({"graph_step_ms": float(np.median(gw)), "kernel_sum_ms": kern_ms,
+                "graph_step_over_kernel_sum": float(np.median(gw)) / kern_ms})
+    del graph
     if all_f:
         ms_f, kind_f = timed("F" * len(roles), max(3, min(steps, 5)))
         res.update({"all_f_step_ms": ms_f, "step_speedup_pattern_vs_allF": ms_f / ms,
@@ -312,6 +475,11 @@ def main():
     import synth
 
     wl = synth.WORKLOADS[args.workload]
+    if args.widened_only:
+        torch.cuda.init()
+        dsa.lib()
+        print(json.dumps({"widened": run_widened_rows()}), flush=True)
+        return
     if wl.decode_B:
         torch.cuda.init()
         dsa.lib()
@@ -514,6 +682,7 @@ def main():
     line["prefill_L32768_bf16"] = cfg1
     line["prefill_L65536_fsssfsss"] = cfg2
     line["decode"] = dec
+    line["widened"] = None if args.no_widened else run_widened_rows()
     print(json.dumps(line), flush=True)
 
 

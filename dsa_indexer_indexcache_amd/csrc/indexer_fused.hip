@@ -219,8 +219,7 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
                                                              const void* __restrict__ k_idx,
                                                              const float* __restrict__ k_scale,
                                                              const uint16_t* __restrict__ w, int H, int k,
-                                                             int64_t n_q, int64_t q_pos0, int64_t k_row0,
-                                                             int64_t n_keys, int block, int bf16_scores,
+                                                             dsa_seqs seqs, int64_t n_groups, int bf16_scores,
                                                              int32_t* __restrict__ idx_out,
                                                              float* __restrict__ score_out) {
   using C = FCfg<FP8, D>;
@@ -228,15 +227,28 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
   __shared__ FusedSmem<FP8, D> sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
-  const int64_t n_groups = (n_q + kFW - 1) / kFW;
-  const int64_t grp = n_groups - 1 - (int64_t)blockIdx.x;  // heaviest rows first
-  const int64_t i0 = grp * kFW;
-  const int64_t i = i0 + wave;
-  const bool row_ok = i < n_q;
-  // last visible key of a row: its position, or its last visible compressed block
-  // (floor(t / block) - 1, -1 for none) with block > 1
+  // Groups of kFW consecutive rows of one sequence (the rows of a group share its key
+  // tiles, so a group never spans two sequences): sequence b owns ceil(nq_b / kFW) groups,
+  // numbered in packed order; the grid takes them from the last (heaviest rows first).
+  const int64_t grp = n_groups - 1 - (int64_t)blockIdx.x;
+  int b = 0;
+  int64_t g0 = 0;
+  for (; b + 1 < seqs.B; ++b) {
+    const int64_t ng = (seqs.q_start[b + 1] - seqs.q_start[b] + kFW - 1) / kFW;
+    if (grp < g0 + ng) break;
+    g0 += ng;
+  }
+  const int64_t n_q = seqs.q_start[b + 1] - seqs.q_start[b];   // rows of this sequence
+  const int64_t q_pos0 = seqs.q_pos0[b], k_row0 = seqs.k_start[b];
+  const int64_t n_keys = seqs.k_start[b + 1] - k_row0;
+  const int block = seqs.block;
+  const int64_t i0 = (grp - g0) * kFW;                        // sequence-local first row
+  const bool row_ok = i0 + wave < n_q;
+  const int64_t i = seqs.q_start[b] + (row_ok ? i0 + wave : n_q - 1);   // packed row
+  // last visible key of a sequence-local row: its position, or its last visible
+  // compressed block (floor(t / block) - 1, -1 for none) with block > 1
   auto last_key = [&](int64_t r) { return block > 1 ? (q_pos0 + r) / block - 1 : q_pos0 + r; };
-  const int64_t t = row_ok ? last_key(i) : -1;
+  const int64_t t = row_ok ? last_key(i0 + wave) : -1;
   const int64_t t_max = last_key(i0 + kFW - 1 < n_q ? i0 + kFW - 1 : n_q - 1);
   constexpr int kTK = FCfg<FP8, D>::tile_keys;
   const int n_tiles = (int)((t_max + kTK) / kTK);
@@ -247,7 +259,7 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
   constexpr int KS = FP8 ? 1 : D / 32;
   i32x4 qa[HB][FP8 ? 2 : KS];
   float wl[HB][4];
-  const int64_t qi = row_ok ? i : n_q - 1;
+  const int64_t qi = i;
   // padded heads (H < 16 HB) read a real head's q and get weight 0
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
@@ -501,25 +513,30 @@ __global__ __launch_bounds__(256) void idx_row_sort_kernel(int32_t* __restrict__
 
 }  // namespace
 
+// Prefill-shaped calls: at least 256 rows and on average at least 8 rows per sequence
+// (a group of 8 rows shares its key tiles; decode-shaped calls, one row per sequence,
+// take the score slab and the wide select instead).
 bool indexer_fused_ok(const IndexerArgs& a) {
-  if (a.seqs.B != 1 || a.k > kSlots * 64) return false;
-  const int64_t n_q = a.seqs.q_start[1] - a.seqs.q_start[0];
-  if (n_q < 256) return false;
+  if (a.k > kSlots * 64) return false;
+  const int64_t n_q = a.seqs.q_start[a.seqs.B] - a.seqs.q_start[0];
+  if (n_q < 256 || n_q < (int64_t)kFW * a.seqs.B) return false;
   if (a.qk_dtype == DSA_FP8_E4M3) return a.d == 128;
   return a.d == 64 || a.d == 128;
 }
 
 hipError_t launch_indexer_fused(const IndexerArgs& a, hipStream_t st) {
-  const int64_t n_q = a.seqs.q_start[1] - a.seqs.q_start[0];
-  const int64_t n_keys = a.seqs.k_start[1] - a.seqs.k_start[0];
+  const int64_t n_q = a.seqs.q_start[a.seqs.B];
+  int64_t n_groups = 0;
+  for (int b = 0; b < a.seqs.B; ++b) n_groups += (a.seqs.q_start[b + 1] - a.seqs.q_start[b] + kFW - 1) / kFW;
+  if (n_groups == 0) return hipSuccess;
   const int HB = a.H <= 16 ? 1 : a.H <= 32 ? 2 : 4;
-  dim3 grid((unsigned)((n_q + kFW - 1) / kFW));
+  dim3 grid((unsigned)n_groups);
   const bool fp8 = a.qk_dtype == DSA_FP8_E4M3;
 #define DSA_FUSED(HBv, F8, Dv)                                                                                 \
   if (HB == HBv && fp8 == F8 && a.d == Dv) {                                                                  \
     hipLaunchKernelGGL((idx_topk_fused_kernel<HBv, F8, Dv>), grid, dim3(64 * kFW), 0, st, a.q_idx, a.q_scale,   \
-                       a.k_idx, a.k_scale, a.w, a.H, a.k, n_q, a.seqs.q_pos0[0], a.seqs.k_start[0], n_keys,  \
-                       a.seqs.block, a.flags & DSA_TOPK_BF16_SCORES, a.idx_out, a.score_out);                \
+                       a.k_idx, a.k_scale, a.w, a.H, a.k, a.seqs, n_groups, a.flags & DSA_TOPK_BF16_SCORES,  \
+                       a.idx_out, a.score_out);                                                              \
     found = true;                                                                                            \
   }
   bool found = false;

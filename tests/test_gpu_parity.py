@@ -184,6 +184,37 @@ def test_attention_random_indices(n_h):
 
 # --------------------------------------------------------------------------- decode (varlen, split attention)
 
+@pytest.mark.parametrize("dtype,integer", [("bf16", True), ("bf16", False), ("fp8", False)])
+def test_packed_varlen_prefill(dtype, integer):
+    """Three ragged sequences in one prefill call (the fused path with per-sequence row
+    groups): a fresh prompt, a chunk continuing at position 500 and a short prompt.  Each
+    sequence's rows equal the same sequence called alone bit for bit, and match the oracle
+    (exactly on integer inputs)."""
+    announce("packed varlen prefill %s%s" % (dtype, " integer" if integer else ""))
+    q_lens, q_pos0 = [700, 1300, 333], [0, 500, 0]
+    k_lens = [p + n for p, n in zip(q_pos0, q_lens)]
+    H, d, k = (16, 64, 97) if integer else (64, 128, 256)
+    li = synth.make_layer(sum(q_lens), sum(k_lens), H, d, 16, wid=15, layer=0, qk_dtype=dtype,
+                          integer_indexer=integer).to(DEV)
+    seqs = dsa.Seqs.varlen(q_lens, k_lens, q_pos0)
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, seqs, q_scale=li.q_scale, k_scale=li.k_scale,
+                               want_scores=True)
+    torch.cuda.synchronize()
+    qa = ka = 0
+    for nq, nk, p0 in zip(q_lens, k_lens, q_pos0):
+        qs = li.q_scale[qa:qa + nq] if li.q_scale is not None else None
+        ks = li.k_scale[ka:ka + nk] if li.k_scale is not None else None
+        one, one_sc = dsa.indexer_topk(li.q_idx[qa:qa + nq], li.k_idx[ka:ka + nk], li.w[qa:qa + nq], k,
+                                       dsa.Seqs.prefill(nq, nk, q_pos0=p0), q_scale=qs, k_scale=ks, want_scores=True)
+        torch.cuda.synchronize()
+        assert torch.equal(one, idx[qa:qa + nq]) and torch.equal(one_sc, sc[qa:qa + nq])
+        qa, ka = qa + nq, ka + nk
+    rows = sorted({0, 1, 7, 8, 96, 699, 700, 701, 1000, 1999, 2000, 2001, 2332} |
+                  set(np.random.default_rng(4).integers(0, sum(q_lens), 40).tolist()))
+    st = check_indexer(OracleView(li), seqs, rows, k, idx, sc, exact=integer)
+    print(st, flush=True)
+
+
 def test_decode_varlen():
     announce("decode varlen")
     lens = [3000, 5000, 4097, 1]
