@@ -468,46 +468,131 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
   }
 }
 
-// Sorts the valid prefix of each index row (positions ascending, scores follow).
-// One workgroup per row; bitonic sort of up to 2048 entries in LDS.
-__global__ __launch_bounds__(256) void idx_row_sort_kernel(int32_t* __restrict__ idx, float* __restrict__ score,
-                                                           int k, int64_t n_q) {
-  __shared__ int32_t sp[2048];
-  __shared__ float ss[2048];
+// Puts the valid prefix of each index row in position order (scores follow).  One
+// workgroup per row.  The entries are distinct positions, so an entry's slot is the number
+// of selected positions below it: a bitmap over the row's position range marks the
+// selection and a prefix sum of its word popcounts gives every entry its slot, with no
+// comparison sort.  Rows whose largest position reaches past the bitmap (2^18 positions)
+// take a bitonic sort in LDS instead.
+constexpr int kOrdThreads = 256;
+constexpr int kOrdWords = 8192;                 // bitmap words: positions < 262144
+constexpr int kOrdPer = 2048 / kOrdThreads;     // entries per thread (k <= 2048)
+
+union OrdSmem {
+  struct {
+    uint32_t bits[kOrdWords];
+    uint32_t pre[kOrdWords];
+  } bm;
+  struct {
+    int32_t sp[2048];
+    float ss[2048];
+  } bt;
+};
+
+__global__ __launch_bounds__(kOrdThreads) void idx_row_order_kernel(int32_t* __restrict__ idx,
+                                                                    float* __restrict__ score, int k, int64_t n_q) {
+  __shared__ OrdSmem sm;
+  __shared__ int32_t red[kOrdThreads / 64];
+  __shared__ uint32_t tot[kOrdThreads / 64];
   const int64_t i = blockIdx.x;
   if (i >= n_q) return;
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   int32_t* row = idx + i * (int64_t)k;
   float* srow = score ? score + i * (int64_t)k : nullptr;
+
+  int32_t p[kOrdPer];
+  float sc[kOrdPer];
+  int32_t mx = -1;
+#pragma unroll
+  for (int u = 0; u < kOrdPer; ++u) {
+    const int j = t + kOrdThreads * u;
+    p[u] = j < k ? row[j] : -1;
+    sc[u] = (j < k && srow) ? srow[j] : 0.f;
+    mx = max(mx, p[u]);
+  }
+  for (int d = 32; d > 0; d >>= 1) mx = max(mx, __shfl_xor(mx, d));
+  if (lane == 0) red[wv] = mx;
+  __syncthreads();
+  mx = max(max(red[0], red[1]), max(red[2], red[3]));
+  if (mx < 0) return;                         // nothing selected: the row is all -1 already
+  const int W = mx / 32 + 1;
+
+  if (W <= kOrdWords) {
+    for (int w = t; w < W; w += kOrdThreads) sm.bm.bits[w] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kOrdPer; ++u)
+      if (p[u] >= 0) atomicOr(&sm.bm.bits[p[u] >> 5], 1u << (p[u] & 31));
+    __syncthreads();
+    // exclusive prefix of the word popcounts: thread t owns words [t c, t c + c)
+    const int c = (W + kOrdThreads - 1) / kOrdThreads;
+    const int w0 = t * c, w1 = min(W, w0 + c);
+    uint32_t own = 0;
+    for (int w = w0; w < w1; ++w) own += __popc(sm.bm.bits[w]);
+    uint32_t incl = own;
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    if (lane == 63) tot[wv] = incl;
+    __syncthreads();
+    uint32_t base = incl - own;
+    for (int w2 = 0; w2 < wv; ++w2) base += tot[w2];
+    for (int w = w0; w < w1; ++w) {
+      sm.bm.pre[w] = base;
+      base += __popc(sm.bm.bits[w]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kOrdPer; ++u) {
+      if (p[u] < 0) continue;
+      const int w = p[u] >> 5;
+      const uint32_t slot = sm.bm.pre[w] + __popc(sm.bm.bits[w] & ((1u << (p[u] & 31)) - 1u));
+      row[slot] = p[u];
+      if (srow) srow[slot] = sc[u];
+    }
+    return;
+  }
+
+  // bitonic fallback over the next power of two >= k
   int n = 1;
   while (n < k) n <<= 1;
-  for (int j = threadIdx.x; j < n; j += blockDim.x) {
-    const int32_t p = j < k ? row[j] : -1;
-    sp[j] = p < 0 ? INT32_MAX : p;
-    ss[j] = (j < k && srow) ? srow[j] : 0.f;
+  for (int j = t; j < n; j += kOrdThreads) {
+    sm.bt.sp[j] = INT32_MAX;
+    sm.bt.ss[j] = 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kOrdPer; ++u) {
+    const int j = t + kOrdThreads * u;
+    if (j < k) {
+      sm.bt.sp[j] = p[u] < 0 ? INT32_MAX : p[u];
+      sm.bt.ss[j] = sc[u];
+    }
   }
   __syncthreads();
   for (int size = 2; size <= n; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int j = threadIdx.x; j < n / 2; j += blockDim.x) {
+      for (int j = t; j < n / 2; j += kOrdThreads) {
         const int lo = 2 * j - (j & (stride - 1));
         const int hi = lo + stride;
         const bool up = (lo & size) == 0;
-        const int32_t a = sp[lo], b = sp[hi];
+        const int32_t a = sm.bt.sp[lo], b = sm.bt.sp[hi];
         if ((a > b) == up) {
-          sp[lo] = b;
-          sp[hi] = a;
-          const float fa = ss[lo];
-          ss[lo] = ss[hi];
-          ss[hi] = fa;
+          sm.bt.sp[lo] = b;
+          sm.bt.sp[hi] = a;
+          const float fa = sm.bt.ss[lo];
+          sm.bt.ss[lo] = sm.bt.ss[hi];
+          sm.bt.ss[hi] = fa;
         }
       }
       __syncthreads();
     }
   }
-  for (int j = threadIdx.x; j < k; j += blockDim.x) {
-    const int32_t p = sp[j];
-    row[j] = p == INT32_MAX ? -1 : p;
-    if (srow) srow[j] = p == INT32_MAX ? 0.f : ss[j];
+  for (int j = t; j < k; j += kOrdThreads) {
+    const int32_t q = sm.bt.sp[j];
+    row[j] = q == INT32_MAX ? -1 : q;
+    if (srow) srow[j] = q == INT32_MAX ? 0.f : sm.bt.ss[j];
   }
 }
 
@@ -547,7 +632,8 @@ hipError_t launch_indexer_fused(const IndexerArgs& a, hipStream_t st) {
   if (!found) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(idx_row_sort_kernel, dim3((unsigned)n_q), dim3(256), 0, st, a.idx_out, a.score_out, a.k, n_q);
+  hipLaunchKernelGGL(idx_row_order_kernel, dim3((unsigned)n_q), dim3(kOrdThreads), 0, st, a.idx_out, a.score_out,
+                     a.k, n_q);
   return hipGetLastError();
 }
 
