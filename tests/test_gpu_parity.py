@@ -215,6 +215,21 @@ def test_packed_varlen_prefill(dtype, integer):
     print(st, flush=True)
 
 
+def test_row_order_past_the_bitmap_range():
+    """Rows whose selected positions reach past 2^18 are put in order by the bitonic fallback
+    instead of the bitmap rank (a 512-row chunk at positions 400000..; checked against the
+    oracle, scores following their positions)."""
+    announce("row order past position 2^18")
+    n_q, p0, k = 512, 400000, 64
+    li = synth.make_layer(n_q, p0 + n_q, 16, 128, 16, wid=16, layer=0, with_attention=False).to(DEV)
+    seqs = dsa.Seqs.prefill(n_q, p0 + n_q, q_pos0=p0)
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, seqs, want_scores=True)
+    torch.cuda.synchronize()
+    rows = [0, 200, 511]
+    st = check_indexer(OracleView(li), seqs, rows, k, idx, sc, exact=False)
+    print(st, flush=True)
+
+
 def test_decode_varlen():
     announce("decode varlen")
     lens = [3000, 5000, 4097, 1]
