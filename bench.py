@@ -319,16 +319,17 @@ def run_widened_rows() -> dict:
         del ca, cb, za, zb, o
 
     # compressed-block selection, prefill: 65,536 query tokens over 16,384 blocks (fp8,
-    # H = 64, d = 128, k = 2048); flops 2 H d per visible (query, block) pair
+    # H = 64, d = 128, the CSA budget k = 1024); flops 2 H d per visible (query, block) pair
+    kc = 1024
     li = synth.make_layer(n, n // m, 64, 128, 16, wid=4, layer=0, qk_dtype="fp8", device=dev, with_attention=False)
     sc = dsa.Seqs.compressed(n, m)
     for bf16s in (False, True):
-        ms = _time_ms(lambda: dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 2048, sc, q_scale=li.q_scale,
+        ms = _time_ms(lambda: dsa.indexer_topk(li.q_idx, li.k_idx, li.w, kc, sc, q_scale=li.q_scale,
                                                k_scale=li.k_scale, bf16_scores=bf16s), reps=3)
         pairs = float((np.arange(n) // m).sum())
         fl = 2.0 * 64 * 128 * pairs
         csa["select_prefill_%s" % ("bf16_scores" if bf16s else "fp32_scores")] = {
-            "queries": n, "blocks": n // m, "k": 2048, "ms": ms, "queries_per_s": n / (ms * 1e-3),
+            "queries": n, "blocks": n // m, "k": kc, "ms": ms, "queries_per_s": n / (ms * 1e-3),
             "tflops": fl / (ms * 1e-3) / 1e12, "frac_fp8_peak": fl / (ms * 1e-3) / PEAK["fp8"]}
     del li
 
@@ -339,17 +340,18 @@ def run_widened_rows() -> dict:
     li = synth.make_layer(8, int(np.sum(nb)), 64, 128, 16, wid=3, layer=0, qk_dtype="bf16", device=dev,
                           with_attention=False)
     sd = dsa.Seqs.varlen([1] * 8, nb, [int(x) - 1 for x in lens], block=m)
-    i32 = torch.empty((8, 2048), dtype=torch.int32, device=dev)
-    i16 = torch.empty_like(i32)
-    ms32 = _time_ms(lambda: dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 2048, sd, idx_out=i32), reps=20)
-    ms16 = _time_ms(lambda: dsa.indexer_topk(li.q_idx, li.k_idx, li.w, 2048, sd, idx_out=i16, bf16_scores=True),
-                    reps=20)
-    cnt = dsa.index_overlap(i16, i32).float()
-    rec = float((cnt / 2048).mean())
     kbytes = 2.0 * 128 * float(np.sum(nb))
-    csa["select_decode_B8"] = {"blocks": nb, "us_fp32_scores": 1e3 * ms32, "us_bf16_scores": 1e3 * ms16,
-                               "key_hbm_frac_fp32": kbytes / (ms32 * 1e-3) / PEAK["hbm"],
-                               "recall_of_fp32_selection_by_bf16": rec}
+    for kc in (512, 1024):
+        i32 = torch.empty((8, kc), dtype=torch.int32, device=dev)
+        i16 = torch.empty_like(i32)
+        ms32 = _time_ms(lambda: dsa.indexer_topk(li.q_idx, li.k_idx, li.w, kc, sd, idx_out=i32), reps=20)
+        ms16 = _time_ms(lambda: dsa.indexer_topk(li.q_idx, li.k_idx, li.w, kc, sd, idx_out=i16,
+                                                 bf16_scores=True), reps=20)
+        cnt = dsa.index_overlap(i16, i32).float()
+        csa["select_decode_B8_k%d" % kc] = {"blocks": nb, "k": kc, "us_fp32_scores": 1e3 * ms32,
+                                           "us_bf16_scores": 1e3 * ms16,
+                                           "key_hbm_frac_fp32": kbytes / (ms32 * 1e-3) / PEAK["hbm"],
+                                           "recall_of_fp32_selection_by_bf16": float((cnt / kc).mean())}
     out["csa"] = csa
     del li
     torch.cuda.synchronize()

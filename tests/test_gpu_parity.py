@@ -244,6 +244,31 @@ def test_decode_varlen():
     check_attention(view, seqs, range(len(lens)), idx, out, 576 ** -0.5)
 
 
+def test_decode_at_the_sequence_limit():
+    """64 sequences (the table's maximum) in one decode call: lengths from 1 to 40000 (the
+    longest take the chunked wide select), k = 2048; selection and attention against the
+    oracle on a sample of rows, every row valid."""
+    announce("decode B=64")
+    g = np.random.default_rng(64)
+    lens = g.integers(1, 12000, size=64)
+    lens[[5, 17, 40]] = [40000, 36000, 33000]
+    lens[9] = 1
+    li = synth.make_layer(64, int(lens.sum()), 64, 128, 128, wid=17, layer=0).to(DEV)
+    seqs = dsa.Seqs.decode(lens)
+    k = 2048
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, seqs, want_scores=True)
+    out = dsa.sparse_attn(li.q, li.latent, idx, seqs)
+    torch.cuda.synchronize()
+    view = OracleView(li)
+    rows = [0, 5, 9, 17, 33, 40, 63]
+    st = check_indexer(view, seqs, rows, k, idx, sc, exact=False)
+    ig = idx.cpu().numpy()
+    for i in range(64):
+        check_valid_row(ig[i], int(lens[i]) - 1, k)
+    worst = check_attention(view, seqs, rows, idx, out, 576 ** -0.5)
+    print(st, "attention error %.2e" % worst, flush=True)
+
+
 def test_decode_wide_select_bf16():
     """Few long rows: the (chunk, row) multi-workgroup select; one row shorter than k."""
     announce("decode wide select bf16")
