@@ -203,3 +203,25 @@ def test_indexcache_loop_over_compressed_keys():
     for l, x in enumerate(layers):
         worst = max(worst, check_attention(OracleView(x), seqs, rows, res.index_cache, res.outs[l], 576 ** -0.5))
     print("worst attention error %.2e" % worst, flush=True)
+
+
+def test_csa_decode_rows_with_nothing_visible():
+    """Decode over compressed caches where some queries see no block yet (t < m) and one sees
+    two: the wide select and the attention handle empty and short rows (all -1, zero output)."""
+    announce("csa decode with empty rows")
+    m, k = 4, 1024
+    lens = [3, 4, 50000, 9]                    # t = 2, 3 -> no block; t = 49999 -> 12499; t = 8 -> 2
+    nb = [L // m for L in lens]
+    li = synth.make_layer(4, int(np.sum(nb)), 64, 128, 16, wid=18, layer=0, device=DEV)
+    seqs = dsa.Seqs.varlen([1] * 4, nb, [L - 1 for L in lens], block=m)
+    idx, sc = dsa.indexer_topk(li.q_idx, li.k_idx, li.w, k, seqs, want_scores=True)
+    out = dsa.sparse_attn(li.q, li.latent, idx, seqs)
+    torch.cuda.synchronize()
+    ig = idx.cpu().numpy()
+    assert np.all(ig[0] == -1) and np.all(ig[1] == -1)
+    assert list(ig[3][:2]) == [0, 1] and np.all(ig[3][2:] == -1)
+    assert float(out[0].abs().max()) == 0.0 and float(out[1].abs().max()) == 0.0
+    view = OracleView(li)
+    st = check_indexer(view, seqs, [0, 1, 2, 3], k, idx, sc, exact=False)
+    worst = check_attention(view, seqs, [2, 3], idx, out, 576 ** -0.5)
+    print(st, "attention error %.2e" % worst, flush=True)
