@@ -96,6 +96,18 @@ int check_indexer(const void* q_idx, const float* q_scale, const void* k_idx, co
   return DSA_OK;
 }
 
+// The attention gather addresses a latent row by a 32-bit byte offset from its sequence's
+// first row: at most (2^32 - 4096) / 1152 rows per sequence.
+constexpr int64_t kMaxLatentRows = (((int64_t)1 << 32) - 4096) / 1152;
+
+int check_latent_rows(const dsa_seqs* s) {
+  for (int b = 0; b < s->B; ++b)
+    if (s->k_start[b + 1] - s->k_start[b] > kMaxLatentRows)
+      return fail(DSA_ERR_UNSUPPORTED, "sequence %d has %lld latent rows (at most %lld per sequence)", b,
+                  (long long)(s->k_start[b + 1] - s->k_start[b]), (long long)kMaxLatentRows);
+  return DSA_OK;
+}
+
 int check_attn(const uint16_t* q, const uint16_t* latent, const int32_t* idx, int n_h, int d_qk, int d_v, int k,
                void* out, int out_dtype, int64_t n_q) {
   if (k < 1) return fail(DSA_ERR_INVALID_ARG, "k=%d < 1", k);
@@ -458,6 +470,8 @@ int dsa_sparse_attn(const uint16_t* q, const uint16_t* latent, const int32_t* id
   if (rc) return rc;
   rc = check_attn(q, latent, idx, n_h, d_qk, d_v, k, out, out_dtype, n_q);
   if (rc) return rc;
+  rc = check_latent_rows(seqs);
+  if (rc) return rc;
   if (n_q == 0) return DSA_OK;
   dsa::AttnArgs a = attn_args(q, latent, idx, n_h, d_qk, d_v, k, scale, *seqs, out, out_dtype);
   const size_t need = dsa::attn_ws_bytes(a);
@@ -519,6 +533,8 @@ int indexcache_forward(const char* roles, const dsa_layer* layers, const dsa_sha
                     shape->d_v, shape->k, L.out, shape->out_dtype, n_q);
     if (rc) return fail(rc, "layer %d: %s", l, g_last_error.c_str());
   }
+  rc = check_latent_rows(seqs);
+  if (rc) return rc;
   if (((uintptr_t)index_cache & 3u) || ((uintptr_t)score_cache & 3u))
     return fail(DSA_ERR_ALIGNMENT, "index/score cache misaligned");
   rc = check_ring(shape->index_rows, n_q, shape->q_chunk, "index_rows");

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/dsa.h"
 
 namespace dsa {
@@ -17,6 +19,15 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// The lane id recomputed where it is used (volatile asm is not hoisted out of loops): for
+// loop-invariant per-lane values that would otherwise stay live across a loop and be
+// spilled under register pressure; two VALU ops instead of a scratch reload.
+__device__ __forceinline__ int lane_id_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
@@ -73,6 +84,33 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+// Compile-time loop: f(std::integral_constant<int, M>) for M = B .. E-1.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// dma16 with a wave-uniform base address (SGPR pair) and a per-lane 32-bit byte offset plus
+// an immediate offset (the copy's scalar-base form): no 64-bit address arithmetic per lane.
+// The instruction's immediate offset moves the LDS destination as well as the global
+// address, so M0 is set IMM bytes below the intended LDS base.
+template <int IMM>
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t lds_base) {
+  static_assert(IMM >= 0 && IMM < 4096, "immediate offset range");
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2 offset:%4\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base) - (uint32_t)IMM), "i"(IMM)
       : "memory");
 }
 __device__ __forceinline__ void dma4(const void* src, uint32_t lds_base) {

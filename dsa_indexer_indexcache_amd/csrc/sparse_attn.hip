@@ -304,7 +304,8 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
                                                                    float* __restrict__ part_o,
                                                                    float* __restrict__ part_ml) {
   __shared__ PairSmem<HG, NW> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: kept in a scalar register, so are the values derived from it
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int nwaves = NW;
   const int pair = wave >> 1, vh = wave & 1;
   const uint32_t n_rb = (uint32_t)((n_q + 7) / 8);  // the grid is 8 n_rb hgroups splits < 2^32 workgroups
@@ -365,15 +366,19 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
     if constexpr (NW % 4 == 0) {
       // copies j = wave + NW m all fill rows 8 (wave % 4) .. +8: one index read, one
       // address; copy m starts NW/4 column groups (16 NW elements) further along the row
-      const int r = 8 * (wave & 3) + lrow;
+      // byte offset from the sequence's first latent row (rows * 1152 B < 2^32 is checked
+      // on the host); copy m adds 32 NW bytes as the instruction's immediate offset
+      const int ln = lane_id_here();
+      const int r = 8 * (wave & 3) + (ln >> 3);
       const int s = sm.idx[blk * kBlk + r];
-      const uint16_t* src0 = lat + (int64_t)(s >= 0 ? s : 0) * kDqk + 8 * (8 * (wave >> 2) + (lpos ^ (r & 7)));
+      const uint32_t off = __umul24((uint32_t)(s >= 0 ? s : 0), 2u * kDqk) +
+                           (uint32_t)(16 * (8 * (wave >> 2) + ((ln & 7) ^ (r & 7))));
       uint8_t* dst0 = &sm.tile[bi][1024 * wave];
-#pragma unroll
-      for (int m_ = 0; m_ < (kTileIns + NW - 1) / NW; ++m_) {
-        if (kTileIns % NW == 0 || wave + NW * m_ < kTileIns)
-          dma16(src0 + 16 * NW * m_, lds_u32(dst0 + 1024 * NW * m_));
-      }
+      static_for<0, (kTileIns + NW - 1) / NW>([&](auto mc) {
+        constexpr int M = decltype(mc)::value;
+        if (kTileIns % NW == 0 || wave + NW * M < kTileIns)
+          dma16_s<32 * NW * M>(lat, off, lds_u32(dst0 + 1024 * NW * M));
+      });
     } else {
       for (int j = wave; j < kTileIns; j += nwaves) {
         const int r = 8 * (j & 3) + lrow;

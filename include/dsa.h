@@ -135,7 +135,9 @@ size_t dsa_indexer_topk_ws(int qk_dtype, int H, int d, int k, const dsa_seqs* se
  *                                   entries outside [0, p] are skipped, never read)
  *   out    [n_q, n_h, d_v]  fp32 or bf16 (out_dtype)  (device, written)
  * A row with no usable index gets out = 0.  Softmax and accumulation are fp32.
- * Supported: n_h in {16,32,64,128}, d_qk == 576, d_v == 512.
+ * Supported: n_h in {16,32,64,128}, d_qk == 576, d_v == 512, at most 3,728,266 latent
+ * rows per sequence (rows are addressed by a 32-bit byte offset; else DSA_ERR_UNSUPPORTED,
+ * also from indexcache_forward).
  */
 int dsa_sparse_attn(const uint16_t* q, const uint16_t* latent, const int32_t* idx, int n_h, int d_qk, int d_v,
                     int k, float scale, const dsa_seqs* seqs /* host */, void* out, int out_dtype, void* ws,

@@ -283,3 +283,14 @@ def test_csa_compress_validation():
     assert f(n=64, b0=16, ca=None) == 0                              # block0 past the last entry: a no-op
     assert f(ca=None) == -1
     assert f(ca=FAKE + 8) == -5
+
+
+def test_attention_rejects_sequences_past_the_latent_offset_range():
+    """Latent rows are addressed by a 32-bit byte offset per sequence: at most
+    (2^32 - 4096) / 1152 rows per sequence."""
+    L = dsa.lib()
+    lim = (2 ** 32 - 4096) // 1152
+    s = dsa.Seqs.decode([lim + 1])
+    rc = L.dsa_sparse_attn(FAKE, FAKE, FAKE, 128, 576, 512, 2048, 0.04, ctypes.byref(s), FAKE, 2, FAKE, 1 << 40,
+                           None)
+    assert rc == -4 and b"latent rows" in L.dsa_last_error()
