@@ -225,7 +225,8 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
   using C = FCfg<FP8, D>;
   constexpr int kRing = ring_of<FP8, D>();
   __shared__ FusedSmem<FP8, D> sm;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: kept in a scalar register, so are the values derived from it
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, g = lane >> 4;
   // Groups of kFW consecutive rows of one sequence (the rows of a group share its key
   // tiles, so a group never spans two sequences): sequence b owns ceil(nq_b / kFW) groups,
@@ -292,13 +293,27 @@ __global__ __launch_bounds__(512) void idx_topk_fused_kernel(const void* __restr
   static_assert(C::dma_per_tile % kFW == 0, "tile copies must spread evenly over the waves");
   auto issue_tile = [&](int T) {
     const int bi = T % kRing;
-    for (int j = wave; j < C::dma_per_tile; j += kFW) {
-      const int r = j * (1024 / C::row_bytes) + lane / C::gran;
-      const int slot = lane % C::gran;
-      int64_t s = (int64_t)T * kTK + r;
-      if (s > n_keys - 1) s = n_keys - 1;  // tail rows past the keys: in-bounds, masked later
-      const uint8_t* src = kbytes + s * C::row_bytes + 16 * (slot ^ (r & 7));
-      dma16(src, lds_u32(&sm.tile[bi][1024 * j]));
+    if ((int64_t)T * kTK + kTK <= n_keys) {
+      // a whole tile of keys: the tile's base is uniform (scalar registers) and each copy
+      // needs only a 32-bit lane offset
+      const uint8_t* tb = kbytes + (int64_t)T * kTK * C::row_bytes;
+      const int ln = lane_id_here();
+#pragma unroll
+      for (int m = 0; m < C::dma_per_tile / kFW; ++m) {
+        const int j = wave + kFW * m;
+        const int r = j * (1024 / C::row_bytes) + ln / C::gran;
+        const uint32_t off = (uint32_t)(r * C::row_bytes + 16 * ((ln % C::gran) ^ (r & 7)));
+        dma16_s<0>(tb, off, lds_u32(&sm.tile[bi][1024 * j]));
+      }
+    } else {
+      for (int j = wave; j < C::dma_per_tile; j += kFW) {
+        const int r = j * (1024 / C::row_bytes) + lane / C::gran;
+        const int slot = lane % C::gran;
+        int64_t s = (int64_t)T * kTK + r;
+        if (s > n_keys - 1) s = n_keys - 1;  // tail rows past the keys: in-bounds, masked later
+        const uint8_t* src = kbytes + s * C::row_bytes + 16 * (slot ^ (r & 7));
+        dma16(src, lds_u32(&sm.tile[bi][1024 * j]));
+      }
     }
     if constexpr (FP8) {
       // wave w copies the scales of keys (kTK/8) w .. of the tile (kTK/8 lanes active)
