@@ -256,10 +256,11 @@ constexpr int kNBuf = 2;
 constexpr int kIdxMax = 2048;
 constexpr int kMaxWaves = 8;
 // Prefetch depths of the paired kernel's LDS reads (QK: 32-column steps; PV: column
-// groups).  Eight waves (two per SIMD, 256 registers each, q and O taking 200) only have
-// room for one step; four waves (one per SIMD) keep several reads in flight.
-template <int NW> constexpr int pf_k() { return NW >= 8 ? 1 : 3; }
-template <int NW> constexpr int pf_v() { return NW >= 8 ? 1 : 2; }
+// groups).  Eight waves (two per SIMD, 256 registers each, q and O taking 200) have room
+// for two steps (three K steps spill and take 30% longer); four waves (one per SIMD) keep
+// more reads in flight.
+template <int NW> constexpr int pf_k() { return NW >= 8 ? 2 : 3; }
+template <int NW> constexpr int pf_v() { return NW >= 8 ? 2 : 2; }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef v4i16 __attribute__((address_space(3))) lds_v4i16;

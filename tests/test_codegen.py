@@ -93,6 +93,35 @@ def test_no_spill_reload_while_lds_copies_are_in_flight(tmp_path, src, kernel):
         assert not _scratch_reload_with_copies_in_flight(body)
 
 
+def _scratch_reload_in_copy_loops(body):
+    """Every scratch reload inside a loop that issues direct-to-LDS copies (a loop-invariant
+    value spilled and reloaded each iteration puts a memory wait on every pass)."""
+    bad = []
+    headers = [(i, l.split(":")[0]) for i, l in enumerate(body) if re.match(r"^\.LBB\S+:", l) and "Loop Header" in l]
+    for h, label in headers:
+        ends = [i for i, l in enumerate(body) if i > h and re.search(r"s_c?branch\w*\s+" + re.escape(label) + r"\b", l)]
+        if not ends:
+            continue
+        seg = body[h:max(ends) + 1]
+        if any("global_load_lds" in l for l in seg):
+            bad += [l.strip() for l in seg if "scratch_load" in l]
+    return bad
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_attention_block_loop_has_no_spill_reload(tmp_path):
+    path = os.path.join(HERE, "..", "dsa_indexer_indexcache_amd", "csrc", "sparse_attn.hip")
+    out = tmp_path / "k.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "--cuda-device-only", "-S", path, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    bodies = _kernel_bodies(out.read_text(), "sparse_attn_pair_kernel")
+    assert len(bodies) == 4
+    for body in bodies:
+        assert not _scratch_reload_in_copy_loops(body)
+
+
 def test_reload_scanner_flags_a_reload_after_a_copy():
     loop = [".LBB0_3:                                ; =>This Inner Loop Header: Depth=1",
             "\ts_waitcnt vmcnt(0)", "\ts_barrier", "\tglobal_load_lds_dwordx4 v[2:3], off",
@@ -101,3 +130,4 @@ def test_reload_scanner_flags_a_reload_after_a_copy():
     assert _scratch_reload_with_copies_in_flight(loop) == ["scratch_load_dword v0, off, off offset:8"]
     ok = loop[:5] + ["\ts_waitcnt vmcnt(0)"] + loop[5:]
     assert _scratch_reload_with_copies_in_flight(ok) == []
+    assert _scratch_reload_in_copy_loops(ok) == ["scratch_load_dword v0, off, off offset:8"]
