@@ -363,23 +363,28 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
   // copy j fills column group j/4, rows 8(j%4) .. +8; lane l lands in row
   // 8(j%4) + l/8 at swizzled position l%8, i.e. it fetches granule (l%8) ^ (row & 7)
   const int lrow = lane >> 3, lpos = lane & 7;
+  // NW % 4 == 0: copies j = wave + NW m all fill rows 8 (wave % 4) .. +8, so one index
+  // read and one byte offset serve all of a wave's copies of a block; copy m starts NW/4
+  // column groups (16 NW elements) further along the row, which is the instruction's
+  // immediate offset (32 NW m bytes).  The offset counts from the sequence's first latent
+  // row (rows * 1152 B < 2^32 is checked on the host).
+  constexpr int kWaveCopies = (kTileIns + NW - 1) / NW;
+  auto gather_off = [&](int blk) -> uint32_t {
+    const int ln = lane_id_here();
+    const int r = 8 * (wave & 3) + (ln >> 3);
+    const int s = sm.idx[blk * kBlk + r];
+    return __umul24((uint32_t)(s >= 0 ? s : 0), 2u * kDqk) +
+           (uint32_t)(16 * (8 * (wave >> 2) + ((ln & 7) ^ (r & 7))));
+  };
+  auto gather_copy = [&](auto mc, uint32_t off, int bi) {
+    constexpr int M = decltype(mc)::value;
+    if (kTileIns % NW == 0 || wave + NW * M < kTileIns)
+      dma16_s<32 * NW * M>(lat, off, lds_u32(&sm.tile[bi][1024 * (wave + NW * M)]));
+  };
   auto gather = [&](int blk, int bi) {
     if constexpr (NW % 4 == 0) {
-      // copies j = wave + NW m all fill rows 8 (wave % 4) .. +8: one index read, one
-      // address; copy m starts NW/4 column groups (16 NW elements) further along the row
-      // byte offset from the sequence's first latent row (rows * 1152 B < 2^32 is checked
-      // on the host); copy m adds 32 NW bytes as the instruction's immediate offset
-      const int ln = lane_id_here();
-      const int r = 8 * (wave & 3) + (ln >> 3);
-      const int s = sm.idx[blk * kBlk + r];
-      const uint32_t off = __umul24((uint32_t)(s >= 0 ? s : 0), 2u * kDqk) +
-                           (uint32_t)(16 * (8 * (wave >> 2) + ((ln & 7) ^ (r & 7))));
-      uint8_t* dst0 = &sm.tile[bi][1024 * wave];
-      static_for<0, (kTileIns + NW - 1) / NW>([&](auto mc) {
-        constexpr int M = decltype(mc)::value;
-        if (kTileIns % NW == 0 || wave + NW * M < kTileIns)
-          dma16_s<32 * NW * M>(lat, off, lds_u32(dst0 + 1024 * NW * M));
-      });
+      const uint32_t off = gather_off(blk);
+      static_for<0, kWaveCopies>([&](auto mc) { gather_copy(mc, off, bi); });
     } else {
       for (int j = wave; j < kTileIns; j += nwaves) {
         const int r = 8 * (j & 3) + lrow;
@@ -399,7 +404,15 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
     // wave's have, and buffer bi^1 (block blk-1) is no longer read.
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
-    if (blk + 1 < blk_hi) gather(blk + 1, bi ^ 1);
+    // The next block's gather: with NW % 4 == 0 its copies are spread over the QK steps
+    // below (issued together they stall the wave until the memory pipeline takes them).
+    const bool more = blk + 1 < blk_hi;
+    uint32_t goff = 0;
+    if constexpr (NW % 4 == 0) {
+      if (more) goff = gather_off(blk + 1);
+    } else {
+      if (more) gather(blk + 1, bi ^ 1);
+    }
     const uint8_t* tile = sm.tile[bi];
 
     // ---- partial S^T over this wave's 288 columns, for two 16-key tiles
@@ -418,9 +431,16 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
     for (int j = 0; j < kPfK; ++j)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) kf[j][kt] = *reinterpret_cast<const i32x4*>(kbase + j * (kBlk * 128) + kt * 2048);
-#pragma unroll
-    for (int ks = 0; ks < 9; ++ks) {
+    // copy m of the next block's gather goes out at step ks = m * 9 / kWaveCopies
+    static_for<0, 9>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NW % 4 == 0) {
+        static_for<0, kWaveCopies>([&](auto mc) {
+          if constexpr (decltype(mc)::value * 9 / kWaveCopies == ks)
+            if (more) gather_copy(mc, goff, bi ^ 1);
+        });
+      }
       if (ks + kPfK < 9) {
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
@@ -432,7 +452,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
 #pragma unroll
         for (int hg = 0; hg < HG; ++hg)
           st[hg][kt] = mfma_bf16_16x16x32(kf[ks % (kPfK + 1)][kt], qf[hg][ks], st[hg][kt]);
-    }
+    });
     __builtin_amdgcn_sched_barrier(0);
     // ---- exchange partial scores with the partner wave
 #pragma unroll
@@ -562,6 +582,317 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
       if (vh == 0 && g == 0) {
         part_ml[(pbase + head0 + 16 * hg + c) * 2 + 0] = m[hg];
         part_ml[(pbase + head0 + 16 * hg + c) * 2 + 1] = lt;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Paired-wave variant for 32 heads per pair (HG = 2), pipelined by one block.
+//
+// The work split of QK and PV is the one above, but the softmax is not computed twice:
+// wave vh normalises only its own 16 heads and hands the other wave its bf16 P and its
+// rescale factor through LDS.  PV of block j runs in the next iteration, after QK of
+// block j + 1: the next block barrier orders the hand-over, the matrix core gets the QK
+// and PV products back to back, and between two blocks there is one exchange barrier and
+// half of the softmax.  Three tile buffers: block j (QK), block j - 1 (PV) and block
+// j + 1 (gather in flight).  In registers, head group 0 is the wave's own (heads
+// 16 vh ..) and group 1 its partner's.  Each O accumulator goes through the same
+// operations in the same order as in the kernel above (rescale by the block's factor,
+// then add its P V), so both kernels give identical results.
+template <int NW>
+struct Pair2Smem {
+  uint8_t tile[3][kTileBytes];
+  f32x4 xs[NW][2][64];  // partial scores of the partner's head group, [wave][key tile][lane]
+  i32x4 px[NW][64];     // a wave's bf16 P of its own heads for the last block, [wave][lane]
+  float pa[NW][64];     // its rescale factor for that block (1 where the running max held)
+  int idx[kIdxMax];
+  float bias[kIdxMax];
+};
+static_assert(sizeof(Pair2Smem<8>) <= 160 * 1024, "LDS of one workgroup");
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void sparse_attn_pair2_kernel(const uint16_t* __restrict__ q,
+                                                                    const uint16_t* __restrict__ latent,
+                                                                    const int32_t* __restrict__ idx, int n_h, int k,
+                                                                    float scale_log2, dsa_seqs seqs, int64_t n_q,
+                                                                    int hgroups, int splits,
+                                                                    float* __restrict__ out_f32,
+                                                                    uint16_t* __restrict__ out_bf16,
+                                                                    float* __restrict__ part_o,
+                                                                    float* __restrict__ part_ml) {
+  __shared__ Pair2Smem<NW> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = wave >> 1, vh = wave & 1;
+  const uint32_t n_rb = (uint32_t)((n_q + 7) / 8);  // same grid order as the kernel above
+  const uint32_t rest = blockIdx.x >> 3;
+  const int hgi = (int)(rest % (uint32_t)hgroups);
+  const uint32_t rs = rest / (uint32_t)hgroups;
+  const int64_t i = (int64_t)(rs % n_rb) * 8 + (blockIdx.x & 7);
+  const int split = (int)(rs / n_rb);
+  if (i >= n_q || split >= splits) return;
+  const int b = seq_of_row(seqs, i);
+  const int64_t p = row_last(seqs, b, i);
+  const uint16_t* lat = latent + seqs.k_start[b] * kDqk;
+  const int c = lane & 15, g = lane >> 4;
+  const int head0 = 16 * NW * hgi + 32 * pair;
+  const int hgl[2] = {vh, vh ^ 1};  // the pair's head group held as register group 0, 1
+
+  const int nblk_total = (k + kBlk - 1) / kBlk;
+  const int per = (nblk_total + splits - 1) / splits;
+  const int blk_lo = min(nblk_total, split * per);
+  const int blk_hi = min(nblk_total, blk_lo + per);
+  const int nblk = blk_hi - blk_lo;
+
+  const int32_t* irow = idx + i * (int64_t)k;
+  for (int j = blk_lo * kBlk + tid; j < blk_hi * kBlk; j += blockDim.x) {
+    const int32_t s = j < k ? irow[j] : -1;
+    const bool ok = s >= 0 && s <= p;
+    sm.idx[j] = ok ? s : -1;
+    sm.bias[j] = ok ? 0.f : -INFINITY;
+  }
+
+  i32x4 qf[2][9];
+#pragma unroll
+  for (int lg = 0; lg < 2; ++lg) {
+    const uint16_t* qrow = q + (i * n_h + head0 + 16 * hgl[lg] + c) * kDqk + 32 * vh + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 9; ++ks) qf[lg][ks] = *reinterpret_cast<const i32x4*>(qrow + 64 * ks);
+  }
+  f32x4 o[2][16];
+#pragma unroll
+  for (int lg = 0; lg < 2; ++lg)
+#pragma unroll
+    for (int vt = 0; vt < 16; ++vt) o[lg][vt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_own = -INFINITY, l_own = 0.f;
+  __syncthreads();
+
+  // gather of block blk into buffer bi, as in the kernel above
+  constexpr int kWaveCopies = (kTileIns + NW - 1) / NW;
+  const int lrow = lane >> 3, lpos = lane & 7;
+  auto gather_off = [&](int blk) -> uint32_t {
+    const int ln = lane_id_here();
+    const int r = 8 * (wave & 3) + (ln >> 3);
+    const int s = sm.idx[blk * kBlk + r];
+    return __umul24((uint32_t)(s >= 0 ? s : 0), 2u * kDqk) +
+           (uint32_t)(16 * (8 * (wave >> 2) + ((ln & 7) ^ (r & 7))));
+  };
+  auto gather_copy = [&](auto mc, uint32_t off, int bi) {
+    constexpr int M = decltype(mc)::value;
+    if (kTileIns % NW == 0 || wave + NW * M < kTileIns)
+      dma16_s<32 * NW * M>(lat, off, lds_u32(&sm.tile[bi][1024 * (wave + NW * M)]));
+  };
+  auto gather = [&](int blk, int bi) {
+    if constexpr (NW % 4 == 0) {
+      const uint32_t off = gather_off(blk);
+      static_for<0, kWaveCopies>([&](auto mc) { gather_copy(mc, off, bi); });
+    } else {
+      for (int j = wave; j < kTileIns; j += NW) {
+        const int r = 8 * (j & 3) + lrow;
+        const int chunk = 8 * (j >> 2) + (lpos ^ (r & 7));
+        const int s = sm.idx[blk * kBlk + r];
+        const uint16_t* src = lat + (int64_t)(s >= 0 ? s : 0) * kDqk + 8 * chunk;
+        dma16(src, lds_u32(&sm.tile[bi][1024 * j]));
+      }
+    }
+  };
+
+  // O += P V of one block for both register groups (P operands pa_[0], pa_[1]); the
+  // partner's group is first rescaled by its owner's factor for that block
+  auto pv_block = [&](const uint8_t* tile) {
+    const i32x4 pown = sm.px[wave][lane];
+    const i32x4 ppar = sm.px[wave ^ 1][lane];
+    const float apar = sm.pa[wave ^ 1][lane];
+    if (__any(apar != 1.f)) {
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = __shfl(apar, 4 * g + r);
+#pragma unroll
+      for (int vt = 0; vt < 16; ++vt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[1][vt][r] *= ar[r];
+    }
+    const int ta = c & 3, tj = c >> 2;
+    const int r0 = 4 * g + tj;
+    const uint8_t* vb0 = tile + r0 * 128 + 16 * ((2 * vh + (ta >> 1)) ^ (r0 & 7)) + 8 * (ta & 1);
+    const uint8_t* vb1 = tile + r0 * 128 + 16 * ((4 + 2 * vh + (ta >> 1)) ^ (r0 & 7)) + 8 * (ta & 1);
+    constexpr int kPfV = pf_v<NW>();
+    v4i16 vr[kPfV + 1][4];
+    auto vread = [&](int it, v4i16 (&d)[4]) {
+      const int cgo = it * (kBlk * 128);
+      d[0] = tr16(vb0 + cgo);
+      d[1] = tr16(vb0 + cgo + 2048);
+      d[2] = tr16(vb1 + cgo);
+      d[3] = tr16(vb1 + cgo + 2048);
+    };
+#pragma unroll
+    for (int j = 0; j < kPfV; ++j) vread(j, vr[j]);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (it + kPfV < 8) vread(it + kPfV, vr[(it + kPfV) % (kPfV + 1)]);
+      const v4i16 (&cur)[4] = vr[it % (kPfV + 1)];
+      const i32x4 vfe = pack_tr4(cur[0], cur[1]);
+      const i32x4 vfo = pack_tr4(cur[2], cur[3]);
+      o[0][2 * it] = mfma_bf16_16x16x32(pown, vfe, o[0][2 * it]);
+      o[0][2 * it + 1] = mfma_bf16_16x16x32(pown, vfo, o[0][2 * it + 1]);
+      o[1][2 * it] = mfma_bf16_16x16x32(ppar, vfe, o[1][2 * it]);
+      o[1][2 * it + 1] = mfma_bf16_16x16x32(ppar, vfo, o[1][2 * it + 1]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (nblk > 0) gather(blk_lo, 0);
+  int bcur = 0;  // buffer of block j; j - 1 in (bcur + 2) % 3, j + 1 in (bcur + 1) % 3
+  for (int j = 0; j < nblk; ++j) {
+    const int blk = blk_lo + j;
+    const int bnext = bcur == 2 ? 0 : bcur + 1;
+    const int bprev = bcur == 0 ? 2 : bcur - 1;
+    // block j's copies landed; every wave's P of block j - 1 is in LDS; buffer bnext
+    // (block j - 2) is no longer read
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    const bool more = j + 1 < nblk;
+    uint32_t goff = 0;
+    if constexpr (NW % 4 == 0) {
+      if (more) goff = gather_off(blk + 1);
+    } else {
+      if (more) gather(blk + 1, bnext);
+    }
+    const uint8_t* tile = sm.tile[bcur];
+
+    // ---- partial S^T of block j over this wave's 288 columns (both head groups)
+    f32x4 st[2][2];
+#pragma unroll
+    for (int lg = 0; lg < 2; ++lg)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) st[lg][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int kPfK = pf_k<NW>();
+    const uint8_t* kbase = tile + c * 128 + 16 * ((4 * vh + g) ^ (c & 7));
+    i32x4 kf[kPfK + 1][2];
+#pragma unroll
+    for (int jj = 0; jj < kPfK; ++jj)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) kf[jj][kt] = *reinterpret_cast<const i32x4*>(kbase + jj * (kBlk * 128) + kt * 2048);
+    static_for<0, 9>([&](auto ksc) {
+      constexpr int ks = decltype(ksc)::value;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NW % 4 == 0) {
+        static_for<0, kWaveCopies>([&](auto mc) {
+          if constexpr (decltype(mc)::value * 9 / kWaveCopies == ks)
+            if (more) gather_copy(mc, goff, bnext);
+        });
+      }
+      if (ks + kPfK < 9) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+          kf[(ks + kPfK) % (kPfK + 1)][kt] =
+              *reinterpret_cast<const i32x4*>(kbase + (ks + kPfK) * (kBlk * 128) + kt * 2048);
+      }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int lg = 0; lg < 2; ++lg)
+          st[lg][kt] = mfma_bf16_16x16x32(kf[ks % (kPfK + 1)][kt], qf[lg][ks], st[lg][kt]);
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    // the partner's group: this wave's partial goes to its owner
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) sm.xs[wave][kt][lane] = st[1][kt];
+
+    // ---- PV of block j - 1
+    if (j > 0) pv_block(sm.tile[bprev]);
+
+    lds_barrier();  // partial scores exchanged (LDS traffic only, not the gather)
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) st[0][kt] += sm.xs[wave ^ 1][kt][lane];
+
+    // ---- online softmax of the own head group (as in the kernel above)
+    f32x4 bias[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) bias[kt] = *reinterpret_cast<const f32x4*>(&sm.bias[blk * kBlk + 16 * kt + 4 * g]);
+    float x[2][4];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[kt][r] = fmaf(st[0][kt][r], scale_log2, bias[kt][r]);
+        bmax = fmaxf(bmax, x[kt][r]);
+      }
+    bmax = max_over_rows(bmax);
+    float alpha = 1.f;
+    if (__any(bmax > m_own + kLazy)) {
+      const float mnew = fmaxf(m_own, bmax);
+      alpha = (m_own == -INFINITY) ? 0.f : exp2f(m_own - mnew);
+      m_own = mnew;
+      l_own *= alpha;
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * g + r);
+#pragma unroll
+      for (int vt = 0; vt < 16; ++vt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[0][vt][r] *= ar[r];
+    }
+    const float mu = (m_own == -INFINITY) ? 0.f : m_own;
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float psum = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int kt = e >> 1, r = 2 * (e & 1);
+      const bf16x2 v = {(__bf16)__builtin_amdgcn_exp2f(x[kt][r] - mu),
+                        (__bf16)__builtin_amdgcn_exp2f(x[kt][r + 1] - mu)};
+      pk[e] = __builtin_bit_cast(uint32_t, v);
+      psum = __builtin_amdgcn_fdot2_f32_bf16(v, ones, psum, false);
+    }
+    l_own += psum;
+    sm.px[wave][lane] = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+    sm.pa[wave][lane] = alpha;
+    bcur = bnext;
+  }
+  __syncthreads();  // the last block's P of every wave is in LDS
+  if (nblk > 0) pv_block(sm.tile[bcur == 0 ? 2 : bcur - 1]);
+
+  // ---- finish: the owner's normaliser (and running max) of each group
+  float lt_own = l_own;
+  lt_own += __shfl_xor(lt_own, 16);
+  lt_own += __shfl_xor(lt_own, 32);
+  sm.xs[wave][0][lane] = f32x4{lt_own, m_own, 0.f, 0.f};
+  __syncthreads();
+  const f32x4 mlp = sm.xs[wave ^ 1][0][lane];
+  const float ltg[2] = {lt_own, mlp[0]};
+#pragma unroll
+  for (int lg = 0; lg < 2; ++lg) {
+    const float lt = ltg[lg];
+    const int hh = head0 + 16 * hgl[lg];
+    if (splits == 1) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float ir = __shfl(inv, 4 * g + r);
+        const int64_t orow = (i * n_h + hh + 4 * g + r) * kDv + 16 * vh + c;
+#pragma unroll
+        for (int vt = 0; vt < 16; ++vt) {
+          const float val = o[lg][vt][r] * ir;
+          if (out_f32)
+            out_f32[orow + 32 * vt] = val;
+          else
+            out_bf16[orow + 32 * vt] = (uint16_t)f32_to_bf16_bits(val);
+        }
+      }
+    } else {
+      const int64_t pbase = (i * splits + split) * (int64_t)n_h;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t orow = (pbase + hh + 4 * g + r) * kDv + 16 * vh + c;
+#pragma unroll
+        for (int vt = 0; vt < 16; ++vt) part_o[orow + 32 * vt] = o[lg][vt][r];
+      }
+      if (lg == 0 && g == 0) {
+        part_ml[(pbase + hh + c) * 2 + 0] = m_own;
+        part_ml[(pbase + hh + c) * 2 + 1] = lt;
       }
     }
   }
@@ -699,15 +1030,19 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
 #define DSA_PAIR(HGv, NWv)                                                                                     \
   hipLaunchKernelGGL((sparse_attn_pair_kernel<HGv, NWv>), grid, dim3(64 * NWv), 0, st, a.q, a.latent, a.idx, \
                      a.n_h, a.k, scale_log2, a.seqs, n_q, pl.hgroups, splits, of, ob, part_o, part_ml)
+#define DSA_PAIR2(NWv)                                                                                        \
+  hipLaunchKernelGGL((sparse_attn_pair2_kernel<NWv>), grid, dim3(64 * NWv), 0, st, a.q, a.latent, a.idx, a.n_h, \
+                     a.k, scale_log2, a.seqs, n_q, pl.hgroups, splits, of, ob, part_o, part_ml)
     if (pl.hg == 1 && pl.nw == 4)
       DSA_PAIR(1, 4);
     else if (pl.nw == 2)
-      DSA_PAIR(2, 2);
+      DSA_PAIR2(2);
     else if (pl.nw == 4)
-      DSA_PAIR(2, 4);
+      DSA_PAIR2(4);
     else
-      DSA_PAIR(2, 8);
+      DSA_PAIR2(8);
 #undef DSA_PAIR
+#undef DSA_PAIR2
   } else {
     // 16 heads per wave: the Q slice (72 VGPRs) and the O accumulator (128) stay
     // resident with two waves per SIMD and no spills.

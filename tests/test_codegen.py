@@ -79,6 +79,7 @@ def _scratch_reload_with_copies_in_flight(body):
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
 @pytest.mark.parametrize("src,kernel", [("sparse_attn.hip", "sparse_attn_pair_kernel"),
+                                        ("sparse_attn.hip", "sparse_attn_pair2_kernel"),
                                         ("indexer_fused.hip", "idx_topk_fused_kernel")])
 def test_no_spill_reload_while_lds_copies_are_in_flight(tmp_path, src, kernel):
     path = os.path.join(HERE, "..", "dsa_indexer_indexcache_amd", "csrc", src)
@@ -116,8 +117,9 @@ def test_attention_block_loop_has_no_spill_reload(tmp_path):
            "-packed-fp32-ops", "--cuda-device-only", "-S", path, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stderr[-2000:]
-    bodies = _kernel_bodies(out.read_text(), "sparse_attn_pair_kernel")
-    assert len(bodies) == 4
+    asm = out.read_text()
+    bodies = _kernel_bodies(asm, "sparse_attn_pair_kernel") + _kernel_bodies(asm, "sparse_attn_pair2_kernel")
+    assert len(bodies) == 4  # 16 heads per pair (decode) and 32 heads per pair with 2, 4 and 8 waves
     for body in bodies:
         assert not _scratch_reload_in_copy_loops(body)
 
