@@ -566,7 +566,7 @@ def main():
                 "avg_launch_ms": dc["ms_per_step"] / max(launches, 1),
                 "work_per_launch_tflop": (attn_flops if dom == "sparse_attn" else idx_flops) / max(launches, 1) / 1e12}
     if dom == "sparse_attn" and args.L is None:
-        rec = traffic_record("sparse_attn.hip", "sparse_attn_pair_kernel", wl.name)
+        rec = traffic_record("sparse_attn.hip", "sparse_attn_pair2_kernel", wl.name)
         if rec is not None:
             roofline["traffic"] = rec["hbm_bytes_per_launch"]
             roofline["traffic_source"] = rec["summary"]
