@@ -600,16 +600,22 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
 // 16 vh ..) and group 1 its partner's.  Each O accumulator goes through the same
 // operations in the same order as in the kernel above (rescale by the block's factor,
 // then add its P V), so both kernels give identical results.
+// With 8 waves, waves w and w + 4 share a SIMD and the first four win the issue
+// arbitration, finishing QK first.  So that one group's softmax overlaps the other's
+// matrix work, waves 0-3 run PV of block j - 1 before the exchange barrier and waves
+// 4-7 after it (each still passes one exchange barrier per block); P and the factor are
+// kept per block parity, because a wave of the second group may write its P of block j
+// while its partner still reads its P of block j - 1.
 template <int NW>
 struct Pair2Smem {
   uint8_t tile[3][kTileBytes];
   f32x4 xs[NW][2][64];  // partial scores of the partner's head group, [wave][key tile][lane]
-  i32x4 px[NW][64];     // a wave's bf16 P of its own heads for the last block, [wave][lane]
-  float pa[NW][64];     // its rescale factor for that block (1 where the running max held)
+  i32x4 px[2][NW][64];  // a wave's bf16 P of its own heads, [block parity][wave][lane]
+  float pa[2][NW][64];  // its rescale factor for that block (1 where the running max held)
   int idx[kIdxMax];
   float bias[kIdxMax];
 };
-static_assert(sizeof(Pair2Smem<8>) <= 160 * 1024, "LDS of one workgroup");
+static_assert(sizeof(Pair2Smem<8>) <= 160 * 1024, "LDS of one workgroup");  // exactly 160 KB at 8 waves
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW) void sparse_attn_pair2_kernel(const uint16_t* __restrict__ q,
@@ -624,6 +630,7 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair2_kernel(const uint16
   __shared__ Pair2Smem<NW> sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = wave >> 1, vh = wave & 1;
+  const bool late = NW == 8 && wave >= 4;  // runs PV after the exchange barrier
   const uint32_t n_rb = (uint32_t)((n_q + 7) / 8);  // same grid order as the kernel above
   const uint32_t rest = blockIdx.x >> 3;
   const int hgi = (int)(rest % (uint32_t)hgroups);
@@ -699,10 +706,10 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair2_kernel(const uint16
 
   // O += P V of one block for both register groups (P operands pa_[0], pa_[1]); the
   // partner's group is first rescaled by its owner's factor for that block
-  auto pv_block = [&](const uint8_t* tile) {
-    const i32x4 pown = sm.px[wave][lane];
-    const i32x4 ppar = sm.px[wave ^ 1][lane];
-    const float apar = sm.pa[wave ^ 1][lane];
+  auto pv_block = [&](const uint8_t* tile, int par) {
+    const i32x4 pown = sm.px[par][wave][lane];
+    const i32x4 ppar = sm.px[par][wave ^ 1][lane];
+    const float apar = sm.pa[par][wave ^ 1][lane];
     if (__any(apar != 1.f)) {
       float ar[4];
 #pragma unroll
@@ -800,10 +807,10 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair2_kernel(const uint16
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) sm.xs[wave][kt][lane] = st[1][kt];
 
-    // ---- PV of block j - 1
-    if (j > 0) pv_block(sm.tile[bprev]);
-
+    // ---- PV of block j - 1 (before or after the exchange barrier: see above)
+    if (!late && j > 0) pv_block(sm.tile[bprev], (j - 1) & 1);
     lds_barrier();  // partial scores exchanged (LDS traffic only, not the gather)
+    if (late && j > 0) pv_block(sm.tile[bprev], (j - 1) & 1);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) st[0][kt] += sm.xs[wave ^ 1][kt][lane];
 
@@ -848,12 +855,12 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair2_kernel(const uint16
       psum = __builtin_amdgcn_fdot2_f32_bf16(v, ones, psum, false);
     }
     l_own += psum;
-    sm.px[wave][lane] = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
-    sm.pa[wave][lane] = alpha;
+    sm.px[j & 1][wave][lane] = i32x4{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+    sm.pa[j & 1][wave][lane] = alpha;
     bcur = bnext;
   }
   __syncthreads();  // the last block's P of every wave is in LDS
-  if (nblk > 0) pv_block(sm.tile[bcur == 0 ? 2 : bcur - 1]);
+  if (nblk > 0) pv_block(sm.tile[bcur == 0 ? 2 : bcur - 1], (nblk - 1) & 1);
 
   // ---- finish: the owner's normaliser (and running max) of each group
   float lt_own = l_own;
