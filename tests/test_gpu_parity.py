@@ -182,6 +182,34 @@ def test_attention_random_indices(n_h):
     assert (out_bf.float() - ref.float()).abs().max().item() <= 2 ** -7 * max(1.0, out.abs().max().item())
 
 
+@pytest.mark.parametrize("n_h", [32, 64, 128])
+def test_attention_many_rows_every_pair_kernel(n_h):
+    """At 512 rows or more each row is one workgroup with every head (32 heads per wave pair,
+    the softmax split between the pair and PV one block behind QK): 2, 4 and 8 waves.
+    601 rows leave a ragged last group of the 8-row grid order; rows mix full, partly
+    padded (-1, out of range, invisible) and empty index lists over 7 blocks of 32."""
+    announce("attention 601 rows n_h=%d" % n_h)
+    L, k = 601, 200
+    li = layer(L, 8, 64, n_h, wid=1, layer_id=4)
+    g = np.random.default_rng(100 + n_h)
+    idx = np.full((L, k), -1, np.int32)
+    for t in range(L):
+        kind = t % 3
+        if kind == 0:
+            m = min(k, t + 1)
+            idx[t, :m] = np.sort(g.choice(t + 1, size=m, replace=False))
+        elif kind == 1:
+            m = int(g.integers(0, k + 1))
+            idx[t, :m] = g.integers(-2, t + 3, size=m)
+    idx_t = torch.from_numpy(idx).to(DEV)
+    seqs = dsa.Seqs.prefill(L)
+    out = dsa.sparse_attn(li.q, li.latent, idx_t, seqs)
+    torch.cuda.synchronize()
+    rows = sorted(set(range(0, L, 11)) | {1, 2, 598, 599, 600})
+    check_attention(OracleView(li), seqs, rows, idx_t, out, 576 ** -0.5)
+    print("checked %d rows" % len(rows), flush=True)
+
+
 # --------------------------------------------------------------------------- decode (varlen, split attention)
 
 @pytest.mark.parametrize("dtype,integer", [("bf16", True), ("bf16", False), ("fp8", False)])
