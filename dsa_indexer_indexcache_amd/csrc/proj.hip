@@ -114,14 +114,20 @@ __device__ void gemm_tile(const uint16_t* __restrict__ x, int64_t n, const uint1
   __syncthreads();
 }
 
-// cos and sin of pos * base^(-2 j / rope_dim), the angle in fp64 (positions reach 2e5
-// radians; fp32 would lose about 1e-2 of the angle)
-__device__ __forceinline__ void rope_angle(int64_t pos, int j, int rope_dim, double log2_base, float* cs, float* sn) {
-  const double inv = exp2(-(2.0 * j / rope_dim) * log2_base);
-  double sd, cd;
-  sincos((double)pos * inv, &sd, &cd);
-  *cs = (float)cd;
-  *sn = (float)sd;
+// Rotary frequencies in turns: f[j] = base^(-2 j / rope_dim) / (2 pi), j < rope_dim / 2,
+// computed once on the host in fp64 and passed by value.
+struct RopeTurns {
+  double f[32];
+};
+
+// cos and sin of the angle pos * base^(-2 j / rope_dim).  The angle in turns is reduced to
+// [-1/2, 1/2] in fp64 (positions reach 2e5 radians, about 3e4 turns: fp32 would lose about
+// 1e-2 of the angle), then the hardware sine and cosine, which take turns, give fp32 values.
+__device__ __forceinline__ void rope_angle(int64_t pos, double turns_per_pos, float* cs, float* sn) {
+  const double a = (double)pos * turns_per_pos;
+  const float f = (float)(a - rint(a));
+  *cs = __builtin_amdgcn_cosf(f);
+  *sn = __builtin_amdgcn_sinf(f);
 }
 
 // Epilogue for the query projection: the tile is one indexer head (128 dims) of 128
@@ -130,7 +136,7 @@ __device__ __forceinline__ void rope_angle(int64_t pos, int j, int rope_dim, dou
 template <int RD>
 __global__ __launch_bounds__(256) void proj_q_kernel(const uint16_t* __restrict__ q_lat, int64_t n, int K,
                                                      const uint16_t* __restrict__ wq, int H,
-                                                     const int32_t* __restrict__ pos, double log2_base,
+                                                     const int32_t* __restrict__ pos, RopeTurns turns,
                                                      uint16_t* __restrict__ q_idx) {
   __shared__ ProjSmem sm;
   const int64_t row0 = (int64_t)blockIdx.x * kPT;
@@ -148,7 +154,7 @@ __global__ __launch_bounds__(256) void proj_q_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < hr; ++j) {
       float cs, sn;
-      rope_angle(p, j, RD, log2_base, &cs, &sn);
+      rope_angle(p, turns.f[j], &cs, &sn);
       const float a = v[j], b = v[j + hr];
       v[j] = a * cs - b * sn;
       v[j + hr] = a * sn + b * cs;
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(256) void proj_kw_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ wk,
                                                       const float* __restrict__ gamma, const float* __restrict__ beta,
                                                       float eps, const uint16_t* __restrict__ ww, int H, float wscale,
-                                                      const int32_t* __restrict__ pos, double log2_base,
+                                                      const int32_t* __restrict__ pos, RopeTurns turns,
                                                       uint16_t* __restrict__ k_idx, uint16_t* __restrict__ w_out) {
   __shared__ ProjSmem sm;
   const int64_t row0 = (int64_t)blockIdx.x * kPT;
@@ -222,7 +228,7 @@ __global__ __launch_bounds__(256) void proj_kw_kernel(const uint16_t* __restrict
 #pragma unroll
     for (int j = 0; j < hr; ++j) {
       float cs, sn;
-      rope_angle(p, j, RD, log2_base, &cs, &sn);
+      rope_angle(p, turns.f[j], &cs, &sn);
       const float a = v[j], b = v[j + hr];
       v[j] = a * cs - b * sn;
       v[j + hr] = a * sn + b * cs;
@@ -262,16 +268,18 @@ __global__ __launch_bounds__(256) void cache_append_kernel(uint8_t* __restrict__
 hipError_t launch_indexer_project(const ProjectArgs& a, hipStream_t st) {
   const dim3 gq((unsigned)((a.n + kPT - 1) / kPT), (unsigned)a.H);
   const dim3 gk((unsigned)((a.n + kPT - 1) / kPT), 2u);
-  const double l2b = log2((double)a.rope_base);
+  RopeTurns turns = {};
+  for (int j = 0; 2 * j < a.rope_dim && j < 32; ++j)
+    turns.f[j] = pow((double)a.rope_base, -2.0 * j / a.rope_dim) / (2.0 * M_PI);
   const float wscale = (float)(1.0 / sqrt((double)a.H) / sqrt((double)kPT));
 #define DSA_PROJ(RDv)                                                                                        \
   if (a.rope_dim == RDv) {                                                                                   \
-    hipLaunchKernelGGL(proj_q_kernel<RDv>, gq, dim3(256), 0, st, a.q_lat, a.n, a.r, a.wq, a.H, a.pos, l2b,   \
+    hipLaunchKernelGGL(proj_q_kernel<RDv>, gq, dim3(256), 0, st, a.q_lat, a.n, a.r, a.wq, a.H, a.pos, turns,   \
                        a.q_idx);                                                                             \
     hipError_t e = hipGetLastError();                                                                        \
     if (e != hipSuccess) return e;                                                                           \
     hipLaunchKernelGGL(proj_kw_kernel<RDv>, gk, dim3(256), 0, st, a.h, a.n, a.hidden, a.wk, a.gamma, a.beta, \
-                       a.eps, a.ww, a.H, wscale, a.pos, l2b, a.k_idx, a.w);                                  \
+                       a.eps, a.ww, a.H, wscale, a.pos, turns, a.k_idx, a.w);                                  \
     return hipGetLastError();                                                                                \
   }
   DSA_PROJ(0) DSA_PROJ(32) DSA_PROJ(64)
