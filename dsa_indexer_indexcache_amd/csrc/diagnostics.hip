@@ -2,10 +2,17 @@
 // (device side of the fp8 setting) and the cross-layer index overlap ([IDX] §8
 // metrics): for every row, the number of valid positions two index tensors share.
 //
-// One workgroup per row.  Row B's valid positions go into an open-addressing hash
+// One workgroup per row.  When row B's valid positions span fewer than 2^18 values (any
+// row over a context of at most 262,144 tokens), they are marked in a bitmap of that
+// span in LDS and row A's valid positions test their bits: no probe loops, and the
+// inserts are fire-and-forget LDS ORs.  Wider rows go into an open-addressing hash
 // table in LDS (linear probing, at least twice as many slots as entries, so every
-// probe sequence ends at an empty slot); row A's valid positions are then looked up
-// and the hits are summed.  Integer work throughout: the count is exact.
+// probe sequence ends at an empty slot) that A's positions look up.  Valid entries of a
+// row are distinct, so either way the hits sum to |A ∩ B|.  Integer work throughout:
+// the count is exact.
+#include <algorithm>
+#include <climits>
+
 #include "dsa_device.h"
 #include "launch.h"
 
@@ -14,6 +21,7 @@ namespace dsa {
 namespace {
 
 constexpr int kOvThreads = 256;
+constexpr int kOvBitmapBits = 1 << 18;  // 32 KB of LDS
 
 __device__ __forceinline__ uint32_t ov_hash(uint32_t v, uint32_t mask) { return (v * 2654435761u) >> 7 & mask; }
 
@@ -22,14 +30,105 @@ __global__ __launch_bounds__(kOvThreads) void idx_overlap_kernel(const int32_t* 
                                                                  int32_t* __restrict__ counts) {
   extern __shared__ int32_t table[];
   __shared__ int32_t wsum[kOvThreads / 64];
+  __shared__ int32_t wmin[kOvThreads / 64], wmax[kOvThreads / 64];
   const int64_t row = blockIdx.x;
+  const int32_t* rb = b + row * (int64_t)k;
+  const int32_t* ra = a + row * (int64_t)k;
+  int cnt = 0;
+
+  // rows of at most 8 x 256 entries stay in registers (both rows loaded up front, so their
+  // latencies overlap); longer rows are read again per pass
+  constexpr int kReg = 8;
+  const bool in_regs = k <= kReg * kOvThreads;
+  int32_t rvb[kReg], rva[kReg];
+  if (in_regs) {
+#pragma unroll
+    for (int m = 0; m < kReg; ++m) {
+      const int j = m * kOvThreads + threadIdx.x;
+      rvb[m] = j < k ? rb[j] : -1;
+      rva[m] = j < k ? ra[j] : -1;
+    }
+  }
+
+  // ---- span of B's valid entries (lo > hi: none)
+  int lo = INT32_MAX, hi = -1;
+  if (in_regs) {
+#pragma unroll
+    for (int m = 0; m < kReg; ++m)
+      if (rvb[m] >= 0) {
+        lo = min(lo, rvb[m]);
+        hi = max(hi, rvb[m]);
+      }
+  } else {
+    for (int j = threadIdx.x; j < k; j += kOvThreads) {
+      const int32_t v = rb[j];
+      if (v >= 0) {
+        lo = min(lo, v);
+        hi = max(hi, v);
+      }
+    }
+  }
+  for (int d = 32; d >= 1; d >>= 1) {
+    lo = min(lo, __shfl_xor(lo, d));
+    hi = max(hi, __shfl_xor(hi, d));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    wmin[threadIdx.x >> 6] = lo;
+    wmax[threadIdx.x >> 6] = hi;
+  }
+  __syncthreads();
+  lo = wmin[0];
+  hi = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kOvThreads / 64; ++w) {
+    lo = min(lo, wmin[w]);
+    hi = max(hi, wmax[w]);
+  }
+  if (lo > hi) {  // no valid entry in B
+    if (threadIdx.x == 0) counts[row] = 0;
+    return;
+  }
+  if ((int64_t)hi - lo < kOvBitmapBits) {
+    // ---- bitmap of [lo, hi]: clear, mark B, test A
+    const int words = ((hi - lo) >> 5) + 1;
+    uint32_t* bm = reinterpret_cast<uint32_t*>(table);
+    for (int j = threadIdx.x; j < words; j += kOvThreads) bm[j] = 0u;
+    __syncthreads();
+    auto mark = [&](int32_t v) {
+      if (v >= 0) atomicOr(&bm[(v - lo) >> 5], 1u << ((v - lo) & 31));
+    };
+    auto test = [&](int32_t v) {
+      return (v >= lo && v <= hi) ? (int)((bm[(v - lo) >> 5] >> ((v - lo) & 31)) & 1u) : 0;
+    };
+    if (in_regs) {
+#pragma unroll
+      for (int m = 0; m < kReg; ++m) mark(rvb[m]);
+    } else {
+      for (int j = threadIdx.x; j < k; j += kOvThreads) mark(rb[j]);
+    }
+    __syncthreads();
+    if (in_regs) {
+#pragma unroll
+      for (int m = 0; m < kReg; ++m) cnt += test(rva[m]);
+    } else {
+      for (int j = threadIdx.x; j < k; j += kOvThreads) cnt += test(ra[j]);
+    }
+    for (int d = 32; d >= 1; d >>= 1) cnt += __shfl_xor(cnt, d);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int tot = 0;
+      for (int w = 0; w < kOvThreads / 64; ++w) tot += wsum[w];
+      counts[row] = tot;
+    }
+    return;
+  }
+
+  // ---- hash table
   const uint32_t mask = (uint32_t)slots - 1u;
   for (int j = threadIdx.x; j < slots; j += kOvThreads) table[j] = -1;
   // 8 entries per thread per pass (coalesced, all loads issued before use); A's
   // entries of the pass are loaded together with B's, ahead of the table barrier
-  const int32_t* rb = b + row * (int64_t)k;
-  const int32_t* ra = a + row * (int64_t)k;
-  int cnt = 0;
   for (int base = 0; base < k; base += 8 * kOvThreads) {
     int32_t vb[8], va[8];
 #pragma unroll
@@ -175,8 +274,8 @@ hipError_t launch_index_overlap(const int32_t* a, const int32_t* b, int64_t n_ro
                                 hipStream_t st) {
   int slots = 64;
   while (slots < 2 * k) slots <<= 1;  // load factor <= 1/2: every probe meets an empty slot
-  hipLaunchKernelGGL(idx_overlap_kernel, dim3((unsigned)n_rows), dim3(kOvThreads), slots * sizeof(int32_t), st, a, b,
-                     k, slots, counts);
+  const size_t lds = std::max((size_t)slots, (size_t)kOvBitmapBits / 32) * sizeof(int32_t);
+  hipLaunchKernelGGL(idx_overlap_kernel, dim3((unsigned)n_rows), dim3(kOvThreads), lds, st, a, b, k, slots, counts);
   return hipGetLastError();
 }
 

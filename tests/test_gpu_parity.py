@@ -442,6 +442,37 @@ def test_index_overlap_exact(n, k):
     assert np.array_equal(got.cpu().numpy(), want)
 
 
+def test_index_overlap_bitmap_and_hash_rows():
+    """Rows whose valid entries of B span fewer than 2^18 positions take the bitmap, wider
+    rows the hash table: both in one call, at the span boundary (2^18 - 1 and 2^18), near
+    INT32_MAX, and with B empty or a single entry."""
+    announce("index overlap bitmap and hash rows")
+    n, k = 60, 2048
+    g = np.random.default_rng(77)
+    a = np.full((n, k), -1, dtype=np.int32)
+    b = np.full((n, k), -1, dtype=np.int32)
+    for i in range(n):
+        mode = i % 5
+        base = 2 ** 31 - 1_000_000 if mode == 3 else 1000
+        span = {0: 4 * k + 7, 1: 2 ** 18, 2: 2 ** 18 + 1, 3: 1_000_000, 4: 4 * k}[mode]
+        pool = base + g.choice(span, size=4 * k, replace=False)
+        if mode in (1, 2):   # B holds both ends: hi - lo = span - 1
+            pool = np.concatenate([[base, base + span - 1], pool[(pool != base) & (pool != base + span - 1)]])
+        va = int(g.integers(0, k + 1))
+        vb = int(g.integers(0, 2)) if mode == 4 else int(g.integers(2, k + 1))
+        common = int(g.integers(0, min(va, vb) + 1))
+        sb = pool[:vb]
+        sa = np.concatenate([sb[:common], pool[vb:vb + va - common]])
+        a[i, :va] = g.permutation(sa)
+        b[i, :vb] = sb if mode in (1, 2) else g.permutation(sb)
+        a[i] = g.permutation(a[i])
+        b[i] = g.permutation(b[i])
+    got = dsa.index_overlap(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV))
+    torch.cuda.synchronize()
+    want = np.array([round(oracle.overlap(a[i], b[i], k) * k) for i in range(n)], dtype=np.int32)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
 def test_index_overlap_between_two_f_layers():
     """Cross-layer overlap of two F layers' own selections (FF stack), against the oracle."""
     announce("index overlap of two F layers")
