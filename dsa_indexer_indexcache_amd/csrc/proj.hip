@@ -17,8 +17,8 @@
 // GEMM core: C[n, N] = X[n, K] . W[N, K]^T (nn.Linear weight layout, both operands
 // K-contiguous), bf16 in, fp32 accumulate, with v_mfma_f32_16x16x32_bf16.  A workgroup
 // of 4 waves computes a 128 x 128 tile (wave (wr, wc) a 64 x 64 quarter: 4 x 4 MFMA
-// tiles); K advances 64 at a time through two LDS stages of 128 rows x 64 columns for
-// each operand, filled by direct global->LDS copies one stage ahead; rows are 128 bytes
+// tiles); K advances 64 at a time through a ring of LDS stages of 128 rows x 64 columns
+// for each operand, filled by direct global->LDS copies stages - 1 ahead; rows are 128 bytes
 // with their eight 16-byte granules XOR-swizzled by (row & 7), so the 16 rows of a
 // fragment read land on distinct banks.  The fp32 tile then goes through LDS to the
 // epilogue, which sees whole 128-column rows (one indexer head, or the key).
@@ -35,10 +35,15 @@ constexpr int kPT = 128;          // tile rows and columns
 constexpr int kPK = 64;           // K per stage
 constexpr int kPStage = kPT * kPK * 2;  // bytes of one operand's stage (16 KB)
 
+// Two stages for the query projection (two workgroups per CU hide the copy latency);
+// four for the key / head-weight projection, whose grid has a workgroup for every 128 rows
+// only and whose K (the hidden size) takes a hundred steps, each of them short next to
+// the latency of the copies it waits for.
+template <int STAGES>
 struct ProjSmem {
   union {
-    uint8_t stage[2][2][kPStage];   // [stage][operand: 0 = X, 1 = W]
-    float tile[kPT][kPT + 1];       // accumulators for the epilogue (+1: no bank conflicts)
+    uint8_t stage[STAGES][2][kPStage];  // [stage][operand: 0 = X, 1 = W]
+    float tile[kPT][kPT + 1];           // accumulators for the epilogue (+1: no bank conflicts)
   };
 };
 
@@ -60,8 +65,9 @@ __device__ __forceinline__ void stage_copy(const uint16_t* __restrict__ m, int64
 }
 
 // The 128 x 128 fp32 tile C[row0 .., col0 ..] of X . W^T into sm.tile (K % 64 == 0).
+template <int STAGES>
 __device__ void gemm_tile(const uint16_t* __restrict__ x, int64_t n, const uint16_t* __restrict__ w, int64_t nout,
-                          int K, int64_t row0, int64_t col0, ProjSmem& sm) {
+                          int K, int64_t row0, int64_t col0, ProjSmem<STAGES>& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = lane & 15, g = lane >> 4;
   const int wr = wave >> 1, wc = wave & 1;
@@ -71,19 +77,31 @@ __device__ void gemm_tile(const uint16_t* __restrict__ x, int64_t n, const uint1
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nst = K / kPK;
-  stage_copy(x, n, K, row0, 0, sm.stage[0][0], wave, lane);
-  stage_copy(w, nout, K, col0, 0, sm.stage[0][1], wave, lane);
+  // each stage is 8 copies per wave (4 per operand): "stage s landed" with later stages
+  // in flight is a fixed vmcnt
+  static_assert(STAGES >= 2 && STAGES <= 4, "vmcnt waits below");
+  for (int s = 0; s < STAGES - 1 && s < nst; ++s) {
+    stage_copy(x, n, K, row0, s * kPK, sm.stage[s][0], wave, lane);
+    stage_copy(w, nout, K, col0, s * kPK, sm.stage[s][1], wave, lane);
+  }
   for (int s = 0; s < nst; ++s) {
-    // this wave's copies of stage s landed; after the barrier every wave's have, and the
-    // other buffer (stage s - 1) is no longer read
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    // this wave's copies of stage s landed; after the barrier every wave's have, and
+    // the buffer of stage s - 1 is no longer read
+    const int later = min(STAGES - 2, nst - 1 - s);
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (s + 1 < nst) {
-      stage_copy(x, n, K, row0, (s + 1) * kPK, sm.stage[(s + 1) & 1][0], wave, lane);
-      stage_copy(w, nout, K, col0, (s + 1) * kPK, sm.stage[(s + 1) & 1][1], wave, lane);
+    const int sn = s + STAGES - 1;
+    if (sn < nst) {
+      stage_copy(x, n, K, row0, sn * kPK, sm.stage[sn % STAGES][0], wave, lane);
+      stage_copy(w, nout, K, col0, sn * kPK, sm.stage[sn % STAGES][1], wave, lane);
     }
-    const uint8_t* xs = sm.stage[s & 1][0];
-    const uint8_t* ws = sm.stage[s & 1][1];
+    const uint8_t* xs = sm.stage[s % STAGES][0];
+    const uint8_t* ws = sm.stage[s % STAGES][1];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       i32x4 af[4], bf[4];
@@ -138,10 +156,10 @@ __global__ __launch_bounds__(256) void proj_q_kernel(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ wq, int H,
                                                      const int32_t* __restrict__ pos, RopeTurns turns,
                                                      uint16_t* __restrict__ q_idx) {
-  __shared__ ProjSmem sm;
+  __shared__ ProjSmem<2> sm;
   const int64_t row0 = (int64_t)blockIdx.x * kPT;
   const int head = blockIdx.y;
-  gemm_tile(q_lat, n, wq, (int64_t)H * kPT, K, row0, (int64_t)head * kPT, sm);
+  gemm_tile<2>(q_lat, n, wq, (int64_t)H * kPT, K, row0, (int64_t)head * kPT, sm);
   const int t = threadIdx.x >> 1, half = threadIdx.x & 1;
   const int64_t row = row0 + t;
   if (row >= n) return;
@@ -180,13 +198,13 @@ __global__ __launch_bounds__(256) void proj_kw_kernel(const uint16_t* __restrict
                                                       float eps, const uint16_t* __restrict__ ww, int H, float wscale,
                                                       const int32_t* __restrict__ pos, RopeTurns turns,
                                                       uint16_t* __restrict__ k_idx, uint16_t* __restrict__ w_out) {
-  __shared__ ProjSmem sm;
+  __shared__ ProjSmem<4> sm;
   const int64_t row0 = (int64_t)blockIdx.x * kPT;
   const bool key = blockIdx.y == 0;
   if (key)
-    gemm_tile(h, n, wk, kPT, K, row0, 0, sm);
+    gemm_tile<4>(h, n, wk, kPT, K, row0, 0, sm);
   else
-    gemm_tile(h, n, ww, H, K, row0, 0, sm);
+    gemm_tile<4>(h, n, ww, H, K, row0, 0, sm);
   const int t = threadIdx.x >> 1, half = threadIdx.x & 1;
   const int64_t row = row0 + t;
   // both threads of a row stay to the end (they exchange partial sums)
