@@ -906,64 +906,63 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair2_kernel(const uint16
 }
 
 // Merge split partials: M = max m_s, L = sum l_s 2^(m_s - M), O = sum O_s 2^(m_s - M) / L.
-// A workgroup of 256 threads takes 4 (row, head) pairs, a wave per pair; lane l streams
-// value columns 4l .. 4l+3 and 256 + 4l .. 256 + 4l + 3 (16-byte loads) over the splits.
+// A wave per (row, head, half of the 512 value columns): lane l streams columns
+// 256 half + 4 l .. + 4 (16-byte loads) over the splits.  The values, maxima and sums of
+// eight splits are loaded before any is used, together with the maxima of the remaining
+// splits, so a call with up to eight splits waits for memory once.  Splits are summed in
+// order.
+constexpr int kCombGroup = 8;
 __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(const float* __restrict__ part_o,
                                                                   const float* __restrict__ part_ml, int n_h,
                                                                   int splits, int64_t n_q, float* __restrict__ out_f32,
                                                                   uint16_t* __restrict__ out_bf16) {
-  const int64_t rh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head)
+  const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (row, head, half)
+  const int half = (int)(wv & 1);
+  const int64_t rh = wv >> 1;
   const int lane = threadIdx.x & 63;
   const int64_t i = rh / n_h;
   const int h = (int)(rh % n_h);
   if (i >= n_q) return;
   const float* ml = part_ml + (i * splits * (int64_t)n_h + h) * 2;
   const int64_t mstride = (int64_t)n_h * 2;
-  float M = -INFINITY;
-  for (int s = 0; s < splits; ++s) M = fmaxf(M, ml[s * mstride]);
-  float L = 0.f;
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  const float* po = part_o + (i * splits * (int64_t)n_h + h) * kDv + 4 * lane;
+  const float* po = part_o + (i * splits * (int64_t)n_h + h) * kDv + 256 * half + 4 * lane;
   const int64_t sstride = (int64_t)n_h * kDv;
-  int s = 0;
-  for (; s + 4 <= splits; s += 4) {  // four splits' loads in flight together
-    f32x4 v0[4], v1[4];
-    float wgt[4];
+  f32x4 v[kCombGroup];
+  float ms[kCombGroup], ls[kCombGroup];
+  auto load_group = [&](int s0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v0[u] = *reinterpret_cast<const f32x4*>(po + (s + u) * sstride);
-      v1[u] = *reinterpret_cast<const f32x4*>(po + (s + u) * sstride + 256);
-    }
+    for (int u = 0; u < kCombGroup; ++u)
+      if (s0 + u < splits) {
+        v[u] = *reinterpret_cast<const f32x4*>(po + (s0 + u) * sstride);
+        ms[u] = ml[(s0 + u) * mstride];
+        ls[u] = ml[(s0 + u) * mstride + 1];
+      }
+  };
+  load_group(0);
+  float M = -INFINITY;
+  for (int s = kCombGroup; s < splits; ++s) M = fmaxf(M, ml[s * mstride]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float ms = ml[(s + u) * mstride];
-      wgt[u] = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      L = fmaf(ml[(s + u) * mstride + 1], wgt[u], L);
-    }
+  for (int u = 0; u < kCombGroup; ++u)
+    if (u < splits) M = fmaxf(M, ms[u]);
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += kCombGroup) {
+    if (s0 > 0) load_group(s0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a0 += v0[u] * wgt[u];
-      a1 += v1[u] * wgt[u];
-    }
-  }
-  for (; s < splits; ++s) {
-    const float ms = ml[s * mstride];
-    const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-    L = fmaf(ml[s * mstride + 1], wgt, L);
-    a0 += *reinterpret_cast<const f32x4*>(po + s * sstride) * wgt;
-    a1 += *reinterpret_cast<const f32x4*>(po + s * sstride + 256) * wgt;
+    for (int u = 0; u < kCombGroup; ++u)
+      if (s0 + u < splits) {
+        const float wgt = ms[u] == -INFINITY ? 0.f : exp2f(ms[u] - M);
+        L = fmaf(ls[u], wgt, L);
+        acc += v[u] * wgt;
+      }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  a0 *= inv;
-  a1 *= inv;
-  const int64_t o = (i * n_h + h) * kDv + 4 * lane;
-  if (out_f32) {
-    *reinterpret_cast<f32x4*>(out_f32 + o) = a0;
-    *reinterpret_cast<f32x4*>(out_f32 + o + 256) = a1;
-  } else {
-    *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(pack_bf16x2(a0[0], a0[1]), pack_bf16x2(a0[2], a0[3]));
-    *reinterpret_cast<uint2*>(out_bf16 + o + 256) = make_uint2(pack_bf16x2(a1[0], a1[1]), pack_bf16x2(a1[2], a1[3]));
-  }
+  acc *= inv;
+  const int64_t o = (i * n_h + h) * kDv + 256 * half + 4 * lane;
+  if (out_f32)
+    *reinterpret_cast<f32x4*>(out_f32 + o) = acc;
+  else
+    *reinterpret_cast<uint2*>(out_bf16 + o) = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
 }
 
 // Work split of one call.  Prefill (many rows): one workgroup per row with every head.
@@ -1058,7 +1057,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3((unsigned)((n_q * a.n_h + 3) / 4)), dim3(256), 0, st, part_o,
+  hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3((unsigned)((2 * n_q * a.n_h + 3) / 4)), dim3(256), 0, st, part_o,
                      part_ml, a.n_h, splits, n_q, out_f32, out_bf16);
   return hipGetLastError();
 }
