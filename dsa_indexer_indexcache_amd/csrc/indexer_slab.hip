@@ -23,12 +23,13 @@ namespace dsa {
 constexpr int kScoreKeysPerWave = 256;
 
 template <int HB, int D>
-__global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __restrict__ q_idx,
+__global__ __launch_bounds__(256, 4) void idx_score_bf16_kernel(const uint16_t* __restrict__ q_idx,
                                                              const uint16_t* __restrict__ k_idx,
                                                              const uint16_t* __restrict__ w, int H, dsa_seqs seqs,
                                                              int64_t n_q, float* __restrict__ slab, int64_t ld,
                                                              int bf16_scores) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform (a scalar register), so are the row and its key base
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t i = (int64_t)blockIdx.y * 4 + wave;
   if (i >= n_q) return;
   const int b = seq_of_row(seqs, i);
@@ -38,9 +39,16 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
   const int64_t krow0 = seqs.k_start[b];
   const int c = lane & 15, g = lane >> 4;
   constexpr int KS = D / 32;
+  // the wave's keys from a uniform base and a 32-bit lane offset (no per-lane 64-bit
+  // address arithmetic); the last visible key relative to the base, at most the chunk's last
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(k_idx + (krow0 + s0) * D);
+  const int rel_last = (int)min<int64_t>(p - s0, kScoreKeysPerWave - 1);
 
   i32x4 a[HB][KS];
-  float wl[HB][4];
+  // head weights of heads 16 hb + 4 g + r kept as bf16 pairs (r = 2 e, 2 e + 1), widened
+  // to fp32 (exactly) where used: eight registers fewer, so four waves fit on a SIMD and
+  // keep more key loads in flight
+  uint32_t wl2[HB][2];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int head = 16 * hb + c;
@@ -52,20 +60,25 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
         a[hb][ks] = i32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hh = 16 * hb + 4 * g + r;
-      wl[hb][r] = hh < H ? bf16_to_f32(w[i * H + hh]) : 0.f;
+    for (int e = 0; e < 2; ++e) {
+      const int hh = 16 * hb + 4 * g + 2 * e;
+      const uint32_t lo = hh < H ? (uint32_t)w[i * H + hh] : 0u;
+      const uint32_t hi = hh + 1 < H ? (uint32_t)w[i * H + hh + 1] : 0u;
+      wl2[hb][e] = lo | (hi << 16);
     }
   }
+  auto wl = [&](int hb, int r) {
+    const uint32_t x = wl2[hb][r >> 1];
+    return __uint_as_float((r & 1) ? (x & 0xFFFF0000u) : (x << 16));
+  };
 
   // 16 keys per step; the keys of step sb + 1 are loaded while step sb is scored.
   // Rows past the visible prefix load row p (in bounds) and are not written.
   const int nsb = (int)min<int64_t>(kScoreKeysPerWave / 16, (p - s0) / 16 + 1);
   auto load = [&](int sb, i32x4 (&bf)[KS]) {
-    const int64_t s = min<int64_t>(s0 + 16 * sb + c, p);
+    const uint32_t off = (uint32_t)min(16 * sb + c, rel_last) * (2 * D) + 16 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      bf[ks] = *reinterpret_cast<const i32x4*>(k_idx + (krow0 + s) * D + 32 * ks + 8 * g);
+    for (int ks = 0; ks < KS; ++ks) bf[ks] = *reinterpret_cast<const i32x4*>(kbase + off + 64 * ks);
   };
   auto score = [&](int sb, const i32x4 (&bf)[KS]) {
     float part = 0.f;
@@ -75,7 +88,7 @@ __global__ __launch_bounds__(256) void idx_score_bf16_kernel(const uint16_t* __r
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) acc = mfma_bf16_16x16x32(a[hb][ks], bf[ks], acc);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part += wl[hb][r] * relu_bits(acc[r]);
+      for (int r = 0; r < 4; ++r) part += wl(hb, r) * relu_bits(acc[r]);
     }
     // sum over the four 16-lane rows (heads 4g + r) by two permlane swaps
     const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
