@@ -73,8 +73,12 @@ __global__ __launch_bounds__(256, 4) void idx_score_bf16_kernel(const uint16_t* 
   };
 
   // 16 keys per step; the keys of step sb + 1 are loaded while step sb is scored.
-  // Rows past the visible prefix load row p (in bounds) and are not written.
+  // Rows past the visible prefix load row p (in bounds) and are not written.  Scores
+  // collect in LDS and leave in one pass at the end: a global store per step would sit
+  // in the same in-order memory counter as the key loads, so that every step's wait for
+  // its keys also waited for the previous step's store.
   const int nsb = (int)min<int64_t>(kScoreKeysPerWave / 16, (p - s0) / 16 + 1);
+  __shared__ float sbuf[4][kScoreKeysPerWave];
   auto load = [&](int sb, i32x4 (&bf)[KS]) {
     const uint32_t off = (uint32_t)min(16 * sb + c, rel_last) * (2 * D) + 16 * g;
 #pragma unroll
@@ -95,9 +99,8 @@ __global__ __launch_bounds__(256, 4) void idx_score_bf16_kernel(const uint16_t* 
     part = __uint_as_float(x[0]) + __uint_as_float(x[1]);
     const auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(part), __float_as_uint(part), false, false);
     part = __uint_as_float(y[0]) + __uint_as_float(y[1]);
-    const int64_t s = s0 + 16 * sb + c;
     if (bf16_scores) part = __uint_as_float(f32_to_bf16_bits(part) << 16);
-    if (g == 0 && s <= p) slab[i * ld + s] = part;
+    if (g == 0) sbuf[wave][16 * sb + c] = part;
   };
   i32x4 bfa[KS], bfb[KS];
   load(0, bfa);
@@ -107,6 +110,19 @@ __global__ __launch_bounds__(256, 4) void idx_score_bf16_kernel(const uint16_t* 
     if (sb + 1 >= nsb) break;
     if (sb + 2 < nsb) load(sb + 2, bfa);
     score(sb + 1, bfb);
+  }
+  // lane l writes the scores of keys s0 + 4 l .. + 3 (one 16-byte store where the whole
+  // group is visible and the row start is 16-byte aligned); the wave reads only its own
+  // LDS row, which its own earlier writes fill (LDS operations of a wave are ordered)
+  const f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[wave][4 * lane]);
+  const int64_t sl = s0 + 4 * lane;
+  float* dst = slab + i * ld + sl;
+  if (sl + 3 <= p && (((i * ld) & 3) == 0)) {
+    *reinterpret_cast<f32x4*>(dst) = v;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (sl + e <= p) dst[e] = v[e];
   }
 }
 
