@@ -49,22 +49,23 @@ __global__ __launch_bounds__(256, 4) void idx_score_bf16_kernel(const uint16_t* 
   // to fp32 (exactly) where used: eight registers fewer, so four waves fit on a SIMD and
   // keep more key loads in flight
   uint32_t wl2[HB][2];
+  // Padded heads (H < 16 HB) load a real head's q and weight from a clamped index and are
+  // zeroed by a select: no load sits in a branch, so the compiler issues them all before
+  // the first wait (a guarded load per weight had cost a memory round trip each).
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int head = 16 * hb + c;
+    const int hq = min(head, H - 1);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (head < H)
-        a[hb][ks] = *reinterpret_cast<const i32x4*>(q_idx + (i * H + head) * D + 32 * ks + 8 * g);
-      else
-        a[hb][ks] = i32x4{0, 0, 0, 0};
+      const i32x4 v = *reinterpret_cast<const i32x4*>(q_idx + (i * H + hq) * D + 32 * ks + 8 * g);
+      a[hb][ks] = head < H ? v : i32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int hh = 16 * hb + 4 * g + 2 * e;
-      const uint32_t lo = hh < H ? (uint32_t)w[i * H + hh] : 0u;
-      const uint32_t hi = hh + 1 < H ? (uint32_t)w[i * H + hh + 1] : 0u;
-      wl2[hb][e] = lo | (hi << 16);
+      const uint32_t lo = w[i * H + min(hh, H - 1)], hi = w[i * H + min(hh + 1, H - 1)];
+      wl2[hb][e] = (hh < H ? lo : 0u) | ((hh + 1 < H ? hi : 0u) << 16);
     }
   }
   auto wl = [&](int hb, int r) {
@@ -150,20 +151,20 @@ __global__ __launch_bounds__(256) void idx_score_fp8_kernel(const uint8_t* __res
 
   i32x8 a[HB];
   float wl[HB][4];
+  // padded heads: clamped loads and a select, no load in a branch (as in the bf16 kernel)
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int head = 16 * hb + c;
-    if (head < H) {
-      const i32x4* src = reinterpret_cast<const i32x4*>(q_idx + (i * H + head) * D + 32 * g);
-      i32x4 lo = src[0], hi = src[1];
-      a[hb] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    } else {
-      a[hb] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-    }
+    const int hq = min(head, H - 1);
+    const i32x4* src = reinterpret_cast<const i32x4*>(q_idx + (i * H + hq) * D + 32 * g);
+    const i32x4 lo = src[0], hi = src[1];
+    a[hb] = head < H ? i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]} : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int hh = 16 * hb + 4 * g + r;
-      wl[hb][r] = hh < H ? bf16_to_f32(w[i * H + hh]) * q_scale[i * H + hh] : 0.f;
+      const int hc = min(hh, H - 1);
+      const float wv = bf16_to_f32(w[i * H + hc]) * q_scale[i * H + hc];
+      wl[hb][r] = hh < H ? wv : 0.f;
     }
   }
 
