@@ -62,6 +62,29 @@ __device__ __forceinline__ int64_t row_len(const dsa_seqs& s, int64_t i) {
   return row_last(s, b, i) + 1;
 }
 
+// Scores of keys sb .. sb + kWPer - 1 of a slab row with n valid keys (0 past the end):
+// four 16-byte loads when the group lies inside the row (its start is 16-byte aligned:
+// the row pitch and sb are multiples of 4), else scalar loads of clamped, in-row
+// positions.  No load sits in a branch of its own, so all are issued before the first
+// wait (a guarded load per key had cost a memory round trip each).
+__device__ __forceinline__ void load_group(const float* row, int64_t sb, int64_t n, float (&v)[kWPer]) {
+  if (sb + kWPer <= n) {
+#pragma unroll
+    for (int q = 0; q < kWPer / 4; ++q) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(row + sb + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+    }
+  } else {
+    const int64_t last = n > 0 ? n - 1 : 0;
+#pragma unroll
+    for (int j = 0; j < kWPer; ++j) {
+      const float x = row[min(sb + j, last)];
+      v[j] = sb + j < n ? x : 0.f;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kWThreads) void wsel_zero_kernel(WideWs w) {
   const int64_t i = blockIdx.x;
   for (int j = threadIdx.x; j < kWBins; j += kWThreads) w.hist[i * kWBins + j] = 0u;
@@ -78,11 +101,13 @@ __global__ __launch_bounds__(kWThreads) void wsel_hist_kernel(const float* __res
   for (int j = threadIdx.x; j < kWBins; j += kWThreads) lh[j] = 0u;
   __syncthreads();
   const float* row = slab + i * ld;
-#pragma unroll 4
-  for (int j = 0; j < kWPer; ++j) {
-    const int64_t s = s0 + j * kWThreads + threadIdx.x;
-    if (s < n) atomicAdd(&lh[order_key(row[s]) >> kWShift1], 1u);
-  }
+  // all loads first (clamped in-row positions, no load in a branch), then the counts
+  float x[kWPer];
+#pragma unroll
+  for (int j = 0; j < kWPer; ++j) x[j] = row[min(s0 + j * kWThreads + threadIdx.x, n - 1)];
+#pragma unroll
+  for (int j = 0; j < kWPer; ++j)
+    if (s0 + j * kWThreads + threadIdx.x < n) atomicAdd(&lh[order_key(x[j]) >> kWShift1], 1u);
   __syncthreads();
   uint32_t* gh = w.hist + i * kWBins;
   for (int j = threadIdx.x; j < kWBins; j += kWThreads)
@@ -153,11 +178,13 @@ __global__ __launch_bounds__(kWThreads) void wsel_collect_kernel(const float* __
   const float* row = slab + i * ld;
   uint32_t key[kWPer];
   uint32_t gt = 0, nc = 0, candm = 0;
+  float x[kWPer];
+  load_group(row, s0 + (int64_t)t * kWPer, n, x);
 #pragma unroll
   for (int j = 0; j < kWPer; ++j) {
     const int64_t s = s0 + (int64_t)t * kWPer + j;
     const bool ok = s < n;
-    key[j] = ok ? order_key(row[s]) : 0u;
+    key[j] = ok ? order_key(x[j]) : 0u;
     const int bin = (int)(key[j] >> kWShift1);
     gt += (ok && bin > d1) ? 1u : 0u;
     const bool cand = ok && bin == d1;
@@ -318,10 +345,10 @@ __global__ __launch_bounds__(kWThreads) void wsel_write_kernel(const float* __re
   const float* row = slab + i * ld;
   float v[kWPer];
   uint32_t selm = 0;
+  load_group(row, s0 + (int64_t)t * kWPer, n, v);
 #pragma unroll
   for (int j = 0; j < kWPer; ++j) {
     const int64_t s = s0 + (int64_t)t * kWPer + j;
-    v[j] = s < n ? row[s] : 0.f;
     bool sel = false;
     if (s < n) {
       const uint32_t key = order_key(v[j]);
