@@ -327,14 +327,16 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
   const int blk_lo = min(nblk_total, split * per);
   const int blk_hi = min(nblk_total, blk_lo + per);
 
-  // this split's part of the row's index list, invisible or out-of-range entries marked -1
+  // this split's part of the row's index list, invisible or out-of-range entries marked -1;
+  // the entries are loaded (clamped positions, no load in a branch), then q, then staged
+  // in LDS, so one wait for memory covers them all
   const int32_t* irow = idx + i * (int64_t)k;
-  for (int j = blk_lo * kBlk + tid; j < blk_hi * kBlk; j += blockDim.x) {
-    const int32_t s = j < k ? irow[j] : -1;
-    const bool ok = s >= 0 && s <= p;
-    sm.idx[j] = ok ? s : -1;
-    sm.bias[j] = ok ? 0.f : -INFINITY;
-  }
+  constexpr int kStage = kIdxMax / (64 * NW);
+  const int j_lo = blk_lo * kBlk, j_hi = blk_hi * kBlk;
+  int32_t sv[kStage];
+#pragma unroll
+  for (int u = 0; u < kStage; ++u)
+    if (j_lo + 64 * NW * u < j_hi) sv[u] = irow[min(j_lo + tid + 64 * NW * u, k - 1)];
 
   // q slice: B operand of QK; lane -> head (16hg + c); this wave takes the 32-column
   // steps 2 ks + vh (columns 64 ks + 32 vh + 8 g .. +8)
@@ -344,6 +346,16 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair_kernel(const uint16_
     const uint16_t* qrow = q + (i * n_h + head0 + 16 * hg + c) * kDqk + 32 * vh + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 9; ++ks) qf[hg][ks] = *reinterpret_cast<const i32x4*>(qrow + 64 * ks);
+  }
+#pragma unroll
+  for (int u = 0; u < kStage; ++u) {
+    const int j = j_lo + tid + 64 * NW * u;
+    if (j < j_hi) {
+      const int32_t s = j < k ? sv[u] : -1;
+      const bool ok = s >= 0 && s <= p;
+      sm.idx[j] = ok ? s : -1;
+      sm.bias[j] = ok ? 0.f : -INFINITY;
+    }
   }
   f32x4 o[HG][16];
 #pragma unroll
@@ -651,12 +663,27 @@ __global__ __launch_bounds__(64 * NW) void sparse_attn_pair2_kernel(const uint16
   const int blk_hi = min(nblk_total, blk_lo + per);
   const int nblk = blk_hi - blk_lo;
 
+  // The split's index entries (at most kIdxMax, kStage per thread) are loaded from clamped
+  // positions with no load in a branch, so one wait for memory covers them all before they
+  // are staged in LDS; q is loaded after that (its latency overlaps the first gather's, and
+  // the entries' registers are free again under the eight-wave register budget).
   const int32_t* irow = idx + i * (int64_t)k;
-  for (int j = blk_lo * kBlk + tid; j < blk_hi * kBlk; j += blockDim.x) {
-    const int32_t s = j < k ? irow[j] : -1;
-    const bool ok = s >= 0 && s <= p;
-    sm.idx[j] = ok ? s : -1;
-    sm.bias[j] = ok ? 0.f : -INFINITY;
+  constexpr int kStage = kIdxMax / (64 * NW);
+  const int j_lo = blk_lo * kBlk, j_hi = blk_hi * kBlk;
+  {
+    int32_t sv[kStage];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) sv[u] = irow[min(j_lo + tid + 64 * NW * u, k - 1)];
+#pragma unroll
+    for (int u = 0; u < kStage; ++u) {
+      const int j = j_lo + tid + 64 * NW * u;
+      if (j < j_hi) {
+        const int32_t s = j < k ? sv[u] : -1;
+        const bool ok = s >= 0 && s <= p;
+        sm.idx[j] = ok ? s : -1;
+        sm.bias[j] = ok ? 0.f : -INFINITY;
+      }
+    }
   }
 
   i32x4 qf[2][9];
