@@ -151,14 +151,17 @@ int run_indexer(const dsa::IndexerArgs& a, void* ws, hipStream_t st) {
     return DSA_OK;
   }
   float* slab = (float*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
-  hipError_t e = dsa::launch_indexer_slab(a, slab, st);
+  const bool wide = dsa::wide_select_ok(a);
+  void* state = slab + a.seqs.q_start[a.seqs.B] * dsa::slab_ld(a.seqs);
+  uint32_t* zero = nullptr;
+  int64_t zero_words = 0;
+  if (wide) dsa::wide_select_zero_region(a, state, &zero, &zero_words);
+  hipError_t e = dsa::launch_indexer_slab(a, slab, st, zero, zero_words);
   if (e != hipSuccess) return hip_fail(e, "indexer score launch");
-  if (dsa::wide_select_ok(a)) {
-    const int64_t n_q = a.seqs.q_start[a.seqs.B];
-    e = dsa::launch_wide_select(a, slab, slab + n_q * dsa::slab_ld(a.seqs), st);
-  } else {
+  if (wide)
+    e = dsa::launch_wide_select(a, slab, state, true, st);
+  else
     e = dsa::launch_topk_select(a, slab, st);
-  }
   if (e != hipSuccess) return hip_fail(e, "top-k select launch");
   return DSA_OK;
 }

@@ -27,7 +27,13 @@ __global__ __launch_bounds__(256, 4) void idx_score_bf16_kernel(const uint16_t* 
                                                              const uint16_t* __restrict__ k_idx,
                                                              const uint16_t* __restrict__ w, int H, dsa_seqs seqs,
                                                              int64_t n_q, float* __restrict__ slab, int64_t ld,
-                                                             int bf16_scores) {
+                                                             int bf16_scores, uint32_t* __restrict__ zero,
+                                                             int64_t zero_words) {
+  // workgroup (0, 0) first clears the wide select's counters and histograms when asked
+  // (zero != null): they are read by the passes after this kernel, and the stream orders
+  // those after every workgroup here (the separate clearing launch is saved)
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int64_t j = threadIdx.x; j < zero_words; j += 256) zero[j] = 0u;
   // the wave index is uniform (a scalar register), so are the row and its key base
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t i = (int64_t)blockIdx.y * 4 + wave;
@@ -137,7 +143,13 @@ __global__ __launch_bounds__(256) void idx_score_fp8_kernel(const uint8_t* __res
                                                             const float* __restrict__ k_scale,
                                                             const uint16_t* __restrict__ w, int H, dsa_seqs seqs,
                                                             int64_t n_q, float* __restrict__ slab, int64_t ld,
-                                                            int bf16_scores) {
+                                                            int bf16_scores, uint32_t* __restrict__ zero,
+                                                            int64_t zero_words) {
+  // workgroup (0, 0) first clears the wide select's counters and histograms when asked
+  // (zero != null): they are read by the passes after this kernel, and the stream orders
+  // those after every workgroup here (the separate clearing launch is saved)
+  if (zero && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int64_t j = threadIdx.x; j < zero_words; j += 256) zero[j] = 0u;
   constexpr int D = 128;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t i = (int64_t)blockIdx.y * 4 + wave;
@@ -342,7 +354,7 @@ int64_t slab_ld(const dsa_seqs& s) {
   return (mx + 3) & ~int64_t(3);
 }
 
-hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st) {
+hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st, uint32_t* zero, int64_t zero_words) {
   const int64_t n_q = a.seqs.q_start[a.seqs.B];
   if (n_q == 0) return hipSuccess;
   const int64_t ld = slab_ld(a.seqs);
@@ -355,7 +367,7 @@ hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st
 #define DSA_SCORE_BF16(HBv, Dv)                                                                        \
   if (HB == HBv && a.d == Dv) {                                                                      \
     hipLaunchKernelGGL((idx_score_bf16_kernel<HBv, Dv>), grid, dim3(256), 0, st, q, kk, a.w, a.H, a.seqs, \
-                       n_q, slab, ld, bf16s);                                                               \
+                       n_q, slab, ld, bf16s, zero, zero_words);                                             \
     return hipGetLastError();                                                                        \
   }
     DSA_SCORE_BF16(1, 64) DSA_SCORE_BF16(1, 128) DSA_SCORE_BF16(2, 64) DSA_SCORE_BF16(2, 128)
@@ -367,7 +379,7 @@ hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st
 #define DSA_SCORE_FP8(HBv)                                                                                 \
   if (HB == HBv && a.d == 128) {                                                                         \
     hipLaunchKernelGGL((idx_score_fp8_kernel<HBv>), grid, dim3(256), 0, st, q, a.q_scale, kk, a.k_scale, a.w, \
-                       a.H, a.seqs, n_q, slab, ld, bf16s);                                                \
+                       a.H, a.seqs, n_q, slab, ld, bf16s, zero, zero_words);                              \
     return hipGetLastError();                                                                            \
   }
     DSA_SCORE_FP8(1) DSA_SCORE_FP8(2) DSA_SCORE_FP8(4)

@@ -34,14 +34,20 @@ struct AttnArgs {
 
 // indexer_slab.hip: scores of every visible (row, key) into a [n_q, ld] fp32 slab, then top-k.
 int64_t slab_ld(const dsa_seqs& s);
-hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st);
+// zero (or null): zero_words 32-bit words that the score kernel clears before its scores are
+// read (the wide select's counters and histograms, wide_select_zero_region).
+hipError_t launch_indexer_slab(const IndexerArgs& a, float* slab, hipStream_t st, uint32_t* zero = nullptr,
+                               int64_t zero_words = 0);
 hipError_t launch_topk_select(const IndexerArgs& a, const float* slab, hipStream_t st);
 
 // topk_wide.hip: top-k of few long slab rows spread over (chunk, row) workgroups;
 // `state` is wide_select_ws() bytes of workspace.
 bool wide_select_ok(const IndexerArgs& a);
 size_t wide_select_ws(const IndexerArgs& a);
-hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* state, hipStream_t st);
+// The select's per-row counters and histograms, one contiguous range of `state` that must be
+// zero when launch_wide_select starts; with zeroed = false it clears them itself first.
+void wide_select_zero_region(const IndexerArgs& a, void* state, uint32_t** begin, int64_t* words);
+hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* state, bool zeroed, hipStream_t st);
 
 // indexer_fused.hip: one-sequence prefill, scores never leave the chip; no workspace.
 bool indexer_fused_ok(const IndexerArgs& a);

@@ -7,7 +7,7 @@
 //
 // One workgroup per row would leave most of the chip idle and serialise the row's
 // passes on one CU.  Instead every row is cut into chunks of kWChunk keys:
-//   zero    : per-row counters;
+//   zero    : per-row counters and histograms (done by the score kernel when it runs first);
 //   hist    : (chunk, row) workgroups histogram the top 11 key bits (2048 bins) in
 //             LDS and add them into the row's global histogram;
 //   collect : every chunk finds the bin d holding the k-th key from that histogram,
@@ -416,14 +416,23 @@ size_t wide_select_ws(const IndexerArgs& a) {
                               2 * mc * sizeof(uint32_t));
 }
 
-hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* state, hipStream_t st) {
+void wide_select_zero_region(const IndexerArgs& a, void* state, uint32_t** begin, int64_t* words) {
+  // meta and hist are adjacent in the carve: the whole range [meta, hist + n_q bins)
+  const int64_t n_q = a.seqs.q_start[a.seqs.B];
+  const WideWs w = carve(a, state);
+  static_assert(sizeof(RowMeta) % 4 == 0, "RowMeta in words");
+  *begin = reinterpret_cast<uint32_t*>(w.meta);
+  *words = n_q * (int64_t)(sizeof(RowMeta) / 4 + kWBins);
+}
+
+hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* state, bool zeroed, hipStream_t st) {
   const int64_t n_q = a.seqs.q_start[a.seqs.B];
   if (n_q == 0) return hipSuccess;
   const int64_t ld = slab_ld(a.seqs);
   const int mc = wide_chunks(a);
   const WideWs w = carve(a, state);
   const dim3 grid((unsigned)mc, (unsigned)n_q);
-  hipLaunchKernelGGL(wsel_zero_kernel, dim3((unsigned)n_q), dim3(kWThreads), 0, st, w);
+  if (!zeroed) hipLaunchKernelGGL(wsel_zero_kernel, dim3((unsigned)n_q), dim3(kWThreads), 0, st, w);
   hipLaunchKernelGGL(wsel_hist_kernel, grid, dim3(kWThreads), 0, st, slab, ld, a.seqs, w);
   hipLaunchKernelGGL(wsel_collect_kernel, grid, dim3(kWThreads), 0, st, slab, ld, a.seqs, a.k, mc, w);
   hipLaunchKernelGGL(wsel_resolve_kernel, dim3((unsigned)n_q), dim3(kWResThreads), 0, st, slab, ld, a.seqs, a.k, mc,
