@@ -118,18 +118,23 @@ __global__ __launch_bounds__(256, 4) void idx_score_bf16_kernel(const uint16_t* 
     if (sb + 2 < nsb) load(sb + 2, bfa);
     score(sb + 1, bfb);
   }
-  // lane l writes the scores of keys s0 + 4 l .. + 3 (one 16-byte store where the whole
-  // group is visible and the row start is 16-byte aligned); the wave reads only its own
-  // LDS row, which its own earlier writes fill (LDS operations of a wave are ordered)
-  const f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[wave][4 * lane]);
-  const int64_t sl = s0 + 4 * lane;
-  float* dst = slab + i * ld + sl;
-  if (sl + 3 <= p && (((i * ld) & 3) == 0)) {
-    *reinterpret_cast<f32x4*>(dst) = v;
-  } else {
+  // in each group of 256 keys lane l writes the scores of keys 4 l .. + 3 (one 16-byte store
+  // where the whole quad is visible and the row start is 16-byte aligned); the wave reads
+  // only its own LDS row, which its own earlier writes fill (LDS operations of a wave are
+  // ordered)
+  static_assert(kScoreKeysPerWave % 256 == 0, "whole groups of 256 keys per wave");
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (sl + e <= p) dst[e] = v[e];
+  for (int gq = 0; gq < kScoreKeysPerWave / 256; ++gq) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(&sbuf[wave][256 * gq + 4 * lane]);
+    const int64_t sl = s0 + 256 * gq + 4 * lane;
+    float* dst = slab + i * ld + sl;
+    if (sl + 3 <= p && (((i * ld) & 3) == 0)) {
+      *reinterpret_cast<f32x4*>(dst) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (sl + e <= p) dst[e] = v[e];
+    }
   }
 }
 
