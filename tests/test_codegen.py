@@ -38,6 +38,33 @@ def test_fused_indexer_has_no_vgpr_spills(tmp_path):
     assert all(v == 0 for v in kernels.values()), kernels
 
 
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
+def test_decode_score_kernel_keeps_four_waves_per_simd(tmp_path):
+    """The decode score pass is bound by how many key loads are in flight: its 64-head bf16
+    instantiation must fit four waves per SIMD (at most 128 VGPRs) without spilling."""
+    src = os.path.join(HERE, "..", "dsa_indexer_indexcache_amd", "csrc", "indexer_slab.hip")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "--cuda-device-only", "-c", src, "-o", str(tmp_path / "k.o"),
+           "-Rpass-analysis=kernel-resource-usage"]
+    r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    stats, name = {}, None
+    for line in r.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        if name and "idx_score_bf16_kernelILi4ELi128" in name:
+            for key in ("VGPRs", "AGPRs", "VGPRs Spill", "Occupancy \\[waves/SIMD\\]"):
+                m = re.search(r"remark:\s+" + key + r": (\d+)", line)
+                if m:
+                    stats[key.split(" ")[0] if key != "VGPRs Spill" else "spill"] = int(m.group(1))
+    assert stats, "no idx_score_bf16_kernel<4, 128> in the resource report"
+    assert stats.get("spill", 0) == 0, stats
+    assert stats["VGPRs"] + stats.get("AGPRs", 0) <= 128, stats
+    assert stats["Occupancy"] >= 4, stats
+
+
 def _kernel_bodies(asm: str, name_part: str):
     """Assembly text of every kernel whose mangled name contains name_part."""
     out, cur = [], None
