@@ -159,7 +159,7 @@ int run_indexer(const dsa::IndexerArgs& a, void* ws, hipStream_t st) {
   hipError_t e = dsa::launch_indexer_slab(a, slab, st, zero, zero_words);
   if (e != hipSuccess) return hip_fail(e, "indexer score launch");
   if (wide)
-    e = dsa::launch_wide_select(a, slab, state, true, st);
+    e = dsa::launch_wide_select(a, slab, state, st);
   else
     e = dsa::launch_topk_select(a, slab, st);
   if (e != hipSuccess) return hip_fail(e, "top-k select launch");

@@ -44,10 +44,10 @@ hipError_t launch_topk_select(const IndexerArgs& a, const float* slab, hipStream
 // `state` is wide_select_ws() bytes of workspace.
 bool wide_select_ok(const IndexerArgs& a);
 size_t wide_select_ws(const IndexerArgs& a);
-// The select's per-row counters and histograms, one contiguous range of `state` that must be
-// zero when launch_wide_select starts; with zeroed = false it clears them itself first.
+// The select's per-row counters and histograms: one contiguous range of `state` that must be
+// zero when launch_wide_select starts (the score pass clears it, see launch_indexer_slab).
 void wide_select_zero_region(const IndexerArgs& a, void* state, uint32_t** begin, int64_t* words);
-hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* state, bool zeroed, hipStream_t st);
+hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* state, hipStream_t st);
 
 // indexer_fused.hip: one-sequence prefill, scores never leave the chip; no workspace.
 bool indexer_fused_ok(const IndexerArgs& a);

@@ -7,7 +7,7 @@
 //
 // One workgroup per row would leave most of the chip idle and serialise the row's
 // passes on one CU.  Instead every row is cut into chunks of kWChunk keys:
-//   zero    : per-row counters and histograms (done by the score kernel when it runs first);
+//   zero    : per-row counters and histograms, cleared by the score kernel (the first workgroup);
 //   hist    : (chunk, row) workgroups histogram the top 11 key bits (2048 bins) in
 //             LDS and add them into the row's global histogram;
 //   collect : every chunk finds the bin d holding the k-th key from that histogram,
@@ -83,12 +83,6 @@ __device__ __forceinline__ void load_group(const float* row, int64_t sb, int64_t
       v[j] = sb + j < n ? x : 0.f;
     }
   }
-}
-
-__global__ __launch_bounds__(kWThreads) void wsel_zero_kernel(WideWs w) {
-  const int64_t i = blockIdx.x;
-  for (int j = threadIdx.x; j < kWBins; j += kWThreads) w.hist[i * kWBins + j] = 0u;
-  if (threadIdx.x == 0) w.meta[i].cand_cnt = 0u;
 }
 
 __global__ __launch_bounds__(kWThreads) void wsel_hist_kernel(const float* __restrict__ slab, int64_t ld,
@@ -425,14 +419,13 @@ void wide_select_zero_region(const IndexerArgs& a, void* state, uint32_t** begin
   *words = n_q * (int64_t)(sizeof(RowMeta) / 4 + kWBins);
 }
 
-hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* state, bool zeroed, hipStream_t st) {
+hipError_t launch_wide_select(const IndexerArgs& a, const float* slab, void* state, hipStream_t st) {
   const int64_t n_q = a.seqs.q_start[a.seqs.B];
   if (n_q == 0) return hipSuccess;
   const int64_t ld = slab_ld(a.seqs);
   const int mc = wide_chunks(a);
   const WideWs w = carve(a, state);
   const dim3 grid((unsigned)mc, (unsigned)n_q);
-  if (!zeroed) hipLaunchKernelGGL(wsel_zero_kernel, dim3((unsigned)n_q), dim3(kWThreads), 0, st, w);
   hipLaunchKernelGGL(wsel_hist_kernel, grid, dim3(kWThreads), 0, st, slab, ld, a.seqs, w);
   hipLaunchKernelGGL(wsel_collect_kernel, grid, dim3(kWThreads), 0, st, slab, ld, a.seqs, a.k, mc, w);
   hipLaunchKernelGGL(wsel_resolve_kernel, dim3((unsigned)n_q), dim3(kWResThreads), 0, st, slab, ld, a.seqs, a.k, mc,
