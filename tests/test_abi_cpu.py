@@ -130,6 +130,21 @@ def test_workspace_queries():
     assert L.indexcache_forward_ws(b"FSSS", ctypes.byref(sh), ctypes.byref(s)) > 0   # 256-row chunks split attention
 
 
+def test_decode_attention_split_plan_every_head_count():
+    """The few-row plan (head groups x index-list splits) for every supported head count and
+    batch: the workspace holds a whole number of fp32 split partials (O, max, sum per head)."""
+    L = dsa.lib()
+    for n_h in (16, 32, 64, 128):
+        for B in (1, 3, 8, 64):
+            dec = dsa.Seqs.decode([5000 + 17 * b for b in range(B)])
+            need = L.dsa_sparse_attn_ws(n_h, 576, 512, 2048, ctypes.byref(dec))
+            per_split = B * n_h * (512 + 2) * 4
+            if need == 0:
+                continue
+            assert (need - 256) % per_split == 0, (n_h, B, need)
+            assert 1 <= (need - 256) // per_split <= 8, (n_h, B, need)  # the combine takes 8 at once
+
+
 def test_forward_validation():
     L = dsa.lib()
     s = dsa.Seqs.prefill(64)
