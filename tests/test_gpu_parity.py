@@ -272,6 +272,27 @@ def test_decode_varlen():
     check_attention(view, seqs, range(len(lens)), idx, out, 576 ** -0.5)
 
 
+@pytest.mark.parametrize("lens,n_h,k", [([5000], 128, 2048), ([5000], 32, 2048), ([3001, 700], 128, 2048),
+                                        ([3001, 700], 64, 512), ([40], 128, 2048)])
+def test_decode_attention_few_rows(lens, n_h, k):
+    """One or two decode rows: the index list is cut into at most 8 splits of whole blocks
+    (a lone 2048-entry row: 8 splits of 8 blocks over 4 head groups), merged by the combine;
+    a 40-key row leaves most of its 2048 slots -1.  Every row against the oracle."""
+    announce("decode attention lens=%s n_h=%d k=%d" % (lens, n_h, k))
+    g = np.random.default_rng(sum(lens) + n_h + k)
+    li = synth.make_layer(len(lens), sum(lens), 64, 128, n_h, wid=5, layer=2).to(DEV)
+    idx = np.full((len(lens), k), -1, np.int32)
+    for b, n in enumerate(lens):
+        m = min(k, n)
+        idx[b, :m] = np.sort(g.choice(n, size=m, replace=False))
+    idx_t = torch.from_numpy(idx).to(DEV)
+    seqs = dsa.Seqs.decode(lens)
+    out = dsa.sparse_attn(li.q, li.latent, idx_t, seqs)
+    torch.cuda.synchronize()
+    worst = check_attention(OracleView(li), seqs, range(len(lens)), idx_t, out, 576 ** -0.5)
+    print("attention error %.2e" % worst, flush=True)
+
+
 def test_decode_at_the_sequence_limit():
     """64 sequences (the table's maximum) in one decode call: lengths from 1 to 40000 (the
     longest take the chunked wide select), k = 2048; selection and attention against the
