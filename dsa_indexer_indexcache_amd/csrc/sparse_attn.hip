@@ -1023,9 +1023,10 @@ AttnPlan attn_plan(const AttnArgs& a) {
     pl.nw = 4;
     pl.hgroups = a.n_h / 32;
   }
-  // about 256 workgroups, but never more splits than the combine reads with one wait for
-  // memory: every split beyond them costs more than its blocks save (with 2048 entries at
-  // one row, 64 one-block splits take 72 us against 24 us for 8 splits of 8 blocks)
+  // about 256 workgroups, and at most 8 splits: past 8, a split's fixed cost in this kernel
+  // outweighs the blocks it takes off each workgroup (one row of 2048 entries: 72 us as 64
+  // one-block splits, 28.5 us as 16, 24 us as 8 splits of 8 blocks); 8 is also the number
+  // of splits the combine reads with one wait for memory
   const int64_t per_split = n_q * pl.hgroups;
   int s = (int)((256 + per_split - 1) / per_split);
   if (s > nblk) s = nblk;
