@@ -273,11 +273,13 @@ def test_decode_varlen():
 
 
 @pytest.mark.parametrize("lens,n_h,k", [([5000], 128, 2048), ([5000], 32, 2048), ([3001, 700], 128, 2048),
-                                        ([3001, 700], 64, 512), ([40], 128, 2048)])
+                                        ([3001, 700], 64, 512), ([40], 128, 2048), ([5000], 128, 100),
+                                        ([3001, 700], 32, 1000)])
 def test_decode_attention_few_rows(lens, n_h, k):
     """One or two decode rows: the index list is cut into at most 8 splits of whole blocks
     (a lone 2048-entry row: 8 splits of 8 blocks over 4 head groups), merged by the combine;
-    a 40-key row leaves most of its 2048 slots -1.  Every row against the oracle."""
+    a 40-key row leaves most of its 2048 slots -1; k = 100 and 1000 end in a partly filled
+    block that falls in the last split.  Every row against the oracle."""
     announce("decode attention lens=%s n_h=%d k=%d" % (lens, n_h, k))
     g = np.random.default_rng(sum(lens) + n_h + k)
     li = synth.make_layer(len(lens), sum(lens), 64, 128, n_h, wid=5, layer=2).to(DEV)
